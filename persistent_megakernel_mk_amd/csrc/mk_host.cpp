@@ -1,0 +1,753 @@
+// Host runtime of the persistent decode megakernel: configuration checks, the step schedule (the
+// phase table the kernel interprets), buffer layout, weight repacking and the step launches. Everything
+// here is plain C++ over the HIP runtime; the C ABI is declared in include/mk.h.
+//
+// The schedule is the device-side layer/op list of the pages' design ("Kimi K3's TPU megakernel: 92
+// layers in one Pallas call, and what 709 tokens a second measures", section "How it maps onto a TPU
+// v7": a layer loop whose body branches on the layer kind; per layer norm, mixer, residual, norm, FFN,
+// residual). It is built once per row count (1..8) at mk_create and copied to device memory at bind.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mk.h"
+#include "mk_internal.h"
+
+using namespace mk;
+
+extern "C" __global__ void mk_step_kernel(StepArgs a);
+extern "C" __global__ void mk_repack_bf16(const uint16_t *src, int64_t rows, int64_t cols, uint4 *dst, int64_t row_off,
+                                          int64_t KF);
+
+namespace {
+
+thread_local std::string g_err;
+
+mk_status fail(mk_status st, const char *fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                           \
+  do {                                                                                          \
+    hipError_t e_ = (expr);                                                                     \
+    if (e_ != hipSuccess) return fail(MK_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+inline int64_t round16(int64_t v) { return align_up(v, 16); }
+
+// One matrix (or vector) inside the packed weight buffer.
+struct Slot {
+  int64_t off = -1;  // bytes
+  int32_t N = 0, K = 0;
+  bool packed = false;  // tile-major MFMA fragments (else natural row-major bf16)
+  int64_t bytes() const { return (int64_t)N * K * 2; }
+};
+
+struct LayerSlots {
+  Slot attn_norm, ffn_norm, mix_in, wo, gu, wd;
+  // row offsets inside mix_in
+  int32_t q_off = 0, k_off = 0, v_off = 0, a_off = 0, b_off = 0;
+  // required tensors (kind bitmask) and loaded tensors
+  uint32_t need = 0, have = 0;
+};
+
+struct Schedule {
+  std::vector<Phase> phases;
+  int32_t part_floats[2] = {0, 0};
+  int32_t n_chunks = 0, chunk = 0;
+};
+
+}  // namespace
+
+struct mk_ctx {
+  mk_config cfg;
+  int device = -1;
+  int G = 0;  // workgroups (compute units)
+  std::vector<LayerSlots> L;
+  Slot embed, final_norm, lm_head;
+  uint32_t global_need = 0, global_have = 0;
+  int64_t packed_bytes = 0;
+  int n_lin = 0, n_resid = 0, max_rows = 1;
+  std::vector<int> lin_index;  // per layer: index among linear-attention layers (-1 otherwise)
+  int mix_stride = 0;
+  Schedule sched[kMaxRows + 1];  // by row count
+  // scratch layout (byte offsets)
+  int64_t o_status = 0, o_bar = 0, o_fin = 0, o_x = 0, o_ss = 0, o_part[2] = {0, 0}, o_mix = 0, o_attn = 0,
+          o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxRows + 1] = {}, scratch_bytes = 0;
+  int64_t kv_bytes = 0, lin_bytes = 0, latent_bytes = 0;
+  // bound buffers
+  bool bound = false;
+  uint8_t *wbuf = nullptr, *scratch = nullptr;
+  mk_buffers bufs;
+  uint32_t epoch = 0;
+  bool needs_reset = false;
+  // per-op baseline graphs
+  hipGraphExec_t graph[kMaxRows + 1] = {};
+  const void *graph_key[kMaxRows + 1] = {};
+};
+
+namespace {
+
+uint32_t kind_bit(int kind) { return 1u << kind; }
+
+mk_status validate(const mk_config *c) {
+  if (!c) return fail(MK_E_ARG, "cfg is NULL");
+  if (c->n_layers < 1 || c->n_layers > MK_MAX_LAYERS) return fail(MK_E_ARG, "n_layers %d out of [1, %d]", c->n_layers, MK_MAX_LAYERS);
+  if (c->hidden <= 0 || c->hidden % 256) return fail(MK_E_UNSUPPORTED, "hidden %d must be a positive multiple of 256", c->hidden);
+  if (c->vocab < 0 || c->vocab % 16) return fail(MK_E_UNSUPPORTED, "vocab %d must be a multiple of 16", c->vocab);
+  if (c->max_batch < 1 || c->max_batch > MK_MAX_BATCH) return fail(MK_E_ARG, "max_batch %d out of [1, %d]", c->max_batch, MK_MAX_BATCH);
+  if (c->max_ctx < 1) return fail(MK_E_ARG, "max_ctx %d", c->max_ctx);
+  if (!(c->eps > 0.0f)) return fail(MK_E_ARG, "eps must be positive");
+  bool any_gqa = false, any_lin = false;
+  for (int l = 0; l < c->n_layers; ++l) {
+    int m = c->mixer[l], f = c->ffn_kind[l];
+    if (m < MK_MIXER_GQA || m > MK_MIXER_MLA) return fail(MK_E_ARG, "layer %d: bad mixer %d", l, m);
+    if (f != MK_FFN_DENSE && f != MK_FFN_MOE) return fail(MK_E_ARG, "layer %d: bad ffn kind %d", l, f);
+    if (m == MK_MIXER_MLA) return fail(MK_E_UNSUPPORTED, "layer %d: latent attention is not built yet", l);
+    if (f == MK_FFN_MOE) return fail(MK_E_UNSUPPORTED, "layer %d: mixture-of-experts FFN is not built yet", l);
+    any_gqa |= m == MK_MIXER_GQA;
+    any_lin |= m == MK_MIXER_GDN || m == MK_MIXER_KDA;
+  }
+  if (c->ffn <= 0 || c->ffn % 256) return fail(MK_E_UNSUPPORTED, "ffn %d must be a positive multiple of 256", c->ffn);
+  if (any_gqa) {
+    if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads)
+      return fail(MK_E_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
+    if (c->head_dim != 64 && c->head_dim != 128) return fail(MK_E_UNSUPPORTED, "head_dim %d (64 or 128 supported)", c->head_dim);
+    if ((c->n_q_heads * c->head_dim) % 256) return fail(MK_E_UNSUPPORTED, "n_q_heads * head_dim must be a multiple of 256");
+    if ((c->n_q_heads / c->n_kv_heads) * kMaxRows > kAttnMaxQ)
+      return fail(MK_E_UNSUPPORTED, "query heads per kv head %d exceed %d", c->n_q_heads / c->n_kv_heads, kAttnMaxQ / kMaxRows);
+    if (!(c->rope_theta > 0.0f)) return fail(MK_E_ARG, "rope_theta must be positive");
+  }
+  if (any_lin) {
+    if (c->d_k != 128 || c->d_v != 128) return fail(MK_E_UNSUPPORTED, "d_k = d_v = 128 supported (got %d, %d)", c->d_k, c->d_v);
+    if (c->lin_heads <= 0 || (c->lin_heads * c->d_v) % 256)
+      return fail(MK_E_UNSUPPORTED, "lin_heads * d_v must be a positive multiple of 256");
+  }
+  return MK_OK;
+}
+
+// Chooses the k-split count of a product: nf = KF / S a multiple of the wave count, the activation
+// fragments of one split within the LDS budget, and the fewest fragment-slots on the busiest
+// workgroup (plus a per-unit overhead of a few fragments for the cross-wave reduction).
+int choose_splits(int T, int KF, int R, int G, int max_S) {
+  int best = -1;
+  double best_cost = 1e300;
+  for (int S = 1; S <= KF / kWaves; ++S) {
+    if (KF % S || (KF / S) % kWaves || S > max_S) continue;
+    const int nf = KF / S;
+    if ((int64_t)nf * 128 * R > kActLdsBudget) continue;
+    const int64_t units = (int64_t)T * S;
+    const int64_t per = (units + G - 1) / G;
+    const double cost = (double)per * (nf / kWaves + 6) + 0.01 * S;
+    if (cost < best_cost) { best_cost = cost; best = S; }
+  }
+  return best;
+}
+
+Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S) {
+  Phase p;
+  memset(&p, 0, sizeof(p));
+  p.type = PH_GEMV;
+  p.w_off = w.off;
+  p.N = w.N;
+  p.K = w.K;
+  p.T = w.N / kTileRows;
+  p.KF = w.K / kFragK;
+  p.S = choose_splits(p.T, p.KF, R, G, max_S);
+  p.nf = p.S > 0 ? p.KF / p.S : 0;
+  p.act = act;
+  p.out = out;
+  return p;
+}
+
+mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
+  const mk_config &f = c->cfg;
+  const int G = c->G;
+  sc.phases.clear();
+  sc.part_floats[0] = sc.part_floats[1] = 0;
+  auto add_gemv = [&](Phase p) -> mk_status {
+    if (p.S <= 0) return fail(MK_E_CAPACITY, "no k-split of a %dx%d product fits the on-chip budget at %d rows", p.N, p.K, R);
+    if (((int64_t)p.T * p.S + G - 1) / G > kMaxUnits) return fail(MK_E_CAPACITY, "%dx%d product: too many units per workgroup", p.N, p.K);
+    const int buf = p.out == OUT_RESID ? 1 : 0;
+    if (!(p.out == OUT_LOGITS && p.S == 1)) sc.part_floats[buf] = std::max(sc.part_floats[buf], p.S * R * p.N);
+    p.dst_part = buf;
+    sc.phases.push_back(p);
+    return MK_OK;
+  };
+  // split-KV chunking: fewest positions on the busiest workgroup
+  if (f.n_q_heads > 0) {
+    const int nseq_max = R;  // decode: R sequences; verify (R = 8): 1 sequence, 8 query rows
+    double best = 1e300;
+    for (int cs = 16; cs <= kAttnMaxChunk; cs += 16) {
+      const int nc = (f.max_ctx + cs - 1) / cs;
+      const int64_t units = (int64_t)nseq_max * f.n_kv_heads * nc;
+      const double cost = (double)((units + G - 1) / G) * (cs + 48);
+      if (cost < best) { best = cost; sc.chunk = cs; sc.n_chunks = nc; }
+    }
+  }
+  Phase e;
+  memset(&e, 0, sizeof(e));
+  e.type = PH_EMBED;
+  e.w_off = c->embed.off;
+  sc.phases.push_back(e);
+  int resid = 0;
+  for (int l = 0; l < f.n_layers; ++l) {
+    const LayerSlots &s = c->L[l];
+    const int m = f.mixer[l];
+    Phase p = gemv_phase(s.mix_in, ACT_NORM, OUT_PART, R, G, 64);
+    p.layer = l;
+    p.gain_off = s.attn_norm.off;
+    if (mk_status st = add_gemv(p)) return st;
+    Phase mx;
+    memset(&mx, 0, sizeof(mx));
+    mx.layer = l;
+    mx.src_part = 0;
+    mx.src_S = p.S;
+    mx.src_N = p.N;
+    mx.q_off = s.q_off; mx.k_off = s.k_off; mx.v_off = s.v_off; mx.a_off = s.a_off; mx.b_off = s.b_off;
+    if (m == MK_MIXER_GQA) {
+      mx.type = PH_ATTN;
+      mx.chunk = sc.chunk;
+      mx.n_chunks = sc.n_chunks;
+      sc.phases.push_back(mx);
+      Phase mg = mx;
+      mg.type = PH_MERGE;
+      sc.phases.push_back(mg);
+    } else {
+      mx.type = PH_DELTA;
+      mx.lin_idx = c->lin_index[l];
+      mx.per_channel_gate = m == MK_MIXER_KDA;
+      sc.phases.push_back(mx);
+    }
+    Phase o = gemv_phase(s.wo, ACT_MIX, OUT_RESID, R, G, 68);
+    o.layer = l;
+    o.cnt_off = (resid++) * (f.hidden / kTileRows);
+    if (mk_status st = add_gemv(o)) return st;
+    Phase gu = gemv_phase(s.gu, ACT_NORM, OUT_PART, R, G, 64);
+    gu.layer = l;
+    gu.gain_off = s.ffn_norm.off;
+    if (mk_status st = add_gemv(gu)) return st;
+    Phase d = gemv_phase(s.wd, ACT_SWIGLU, OUT_RESID, R, G, 68);
+    d.layer = l;
+    d.src_part = 0;
+    d.src_S = gu.S;
+    d.src_N = gu.N;
+    d.cnt_off = (resid++) * (f.hidden / kTileRows);
+    if (mk_status st = add_gemv(d)) return st;
+  }
+  c->n_resid = resid;
+  if (f.vocab > 0) {
+    Phase lm = gemv_phase(c->lm_head, ACT_NORM, OUT_LOGITS, R, G, 68);
+    lm.gain_off = c->final_norm.off;
+    lm.cnt_off = resid * (f.hidden / kTileRows);  // finalizer counters after the residual ones
+    if (mk_status st = add_gemv(lm)) return st;
+    Phase fin;
+    memset(&fin, 0, sizeof(fin));
+    fin.type = PH_FINAL;
+    sc.phases.push_back(fin);
+  } else {
+    Phase ho;
+    memset(&ho, 0, sizeof(ho));
+    ho.type = PH_HIDDEN_OUT;
+    sc.phases.push_back(ho);
+  }
+  return MK_OK;
+}
+
+mk_status layout(mk_ctx *c) {
+  const mk_config &f = c->cfg;
+  const int H = f.hidden;
+  int64_t off = 0;
+  auto place = [&](Slot &s, int N, int K, bool packed) {
+    s.N = N;
+    s.K = K;
+    s.packed = packed;
+    s.off = off;
+    off = align_up(off + s.bytes(), 256);
+  };
+  c->L.assign(f.n_layers, LayerSlots());
+  c->lin_index.assign(f.n_layers, -1);
+  c->n_lin = 0;
+  int mix_w = 0;
+  if (f.vocab > 0) {
+    place(c->embed, f.vocab, H, false);
+    c->global_need = kind_bit(MK_W_EMBED) | kind_bit(MK_W_FINAL_NORM) | kind_bit(MK_W_LM_HEAD);
+  }
+  for (int l = 0; l < f.n_layers; ++l) {
+    LayerSlots &s = c->L[l];
+    place(s.attn_norm, 1, H, false);
+    place(s.ffn_norm, 1, H, false);
+    const int m = f.mixer[l];
+    int rows, inner;
+    if (m == MK_MIXER_GQA) {
+      s.q_off = 0;
+      s.k_off = f.n_q_heads * f.head_dim;
+      s.v_off = s.k_off + f.n_kv_heads * f.head_dim;
+      rows = s.v_off + f.n_kv_heads * f.head_dim;
+      inner = f.n_q_heads * f.head_dim;
+      s.need = kind_bit(MK_W_Q) | kind_bit(MK_W_K) | kind_bit(MK_W_V) | kind_bit(MK_W_O);
+    } else {
+      const int hk = f.lin_heads * f.d_k;
+      s.q_off = 0;
+      s.k_off = hk;
+      s.v_off = 2 * hk;
+      s.a_off = (int)round16(s.v_off + f.lin_heads * f.d_v);
+      s.b_off = (int)round16(s.a_off + (m == MK_MIXER_KDA ? hk : f.lin_heads));
+      rows = (int)round16(s.b_off + f.lin_heads);
+      inner = f.lin_heads * f.d_v;
+      s.need = kind_bit(MK_W_Q) | kind_bit(MK_W_K) | kind_bit(MK_W_V) | kind_bit(MK_W_A) | kind_bit(MK_W_B) |
+               kind_bit(MK_W_O);
+      c->lin_index[l] = c->n_lin++;
+    }
+    s.need |= kind_bit(MK_W_ATTN_NORM) | kind_bit(MK_W_FFN_NORM) | kind_bit(MK_W_GATE) | kind_bit(MK_W_UP) |
+              kind_bit(MK_W_DOWN);
+    mix_w = std::max(mix_w, inner);
+    place(s.mix_in, rows, H, true);
+    place(s.wo, H, inner, true);
+    place(s.gu, 2 * f.ffn, H, true);
+    place(s.wd, H, f.ffn, true);
+  }
+  if (f.vocab > 0) {
+    place(c->final_norm, 1, H, false);
+    place(c->lm_head, f.vocab, H, true);
+  }
+  c->packed_bytes = off;
+  c->mix_stride = (int)align_up(mix_w, 64);
+  return MK_OK;
+}
+
+mk_status scratch_layout(mk_ctx *c) {
+  const mk_config &f = c->cfg;
+  const int R = c->max_rows, H = f.hidden, G = c->G;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t o = off;
+    off = align_up(off + std::max<int64_t>(bytes, 0), 256);
+    return o;
+  };
+  int64_t part[2] = {0, 0}, attn = 0;
+  for (int r = 1; r <= kMaxRows; ++r) {
+    const Schedule &s = c->sched[r];
+    if (s.phases.empty()) continue;
+    part[0] = std::max<int64_t>(part[0], s.part_floats[0]);
+    part[1] = std::max<int64_t>(part[1], s.part_floats[1]);
+    if (f.n_q_heads > 0) attn = std::max<int64_t>(attn, (int64_t)r * f.n_q_heads * s.n_chunks * (f.head_dim + 2));
+  }
+  c->o_status = take(256);
+  c->o_bar = take(9 * 128);
+  c->o_fin = take(((int64_t)c->n_resid * (H / kTileRows) + f.vocab / kTileRows) * 4);
+  c->o_x = take((int64_t)R * H * 4);
+  c->o_ss = take((int64_t)R * (H / kTileRows) * 4);
+  c->o_part[0] = take(part[0] * 4);
+  c->o_part[1] = take(part[1] * 4);
+  c->o_mix = take((int64_t)R * c->mix_stride * 4);
+  c->o_attn = take(attn * 4);
+  c->o_cand = take((int64_t)G * R * 2 * 4);
+  c->o_rope = take(f.n_q_heads > 0 ? (int64_t)f.max_ctx * (f.head_dim / 2) * 2 * 4 : 0);
+  c->o_snap = take(f.vocab > 0 ? (int64_t)c->n_lin * kMaxRows * f.lin_heads * f.d_v * f.d_k * 4 : 0);
+  c->o_ptrs = take((int64_t)(3 * MK_MAX_LAYERS + MK_MAX_LAYERS) * 8);
+  for (int r = 1; r <= kMaxRows; ++r)
+    if (!c->sched[r].phases.empty()) c->o_phases[r] = take((int64_t)c->sched[r].phases.size() * sizeof(Phase));
+  c->scratch_bytes = off;
+  c->kv_bytes = (int64_t)f.max_batch * f.n_kv_heads * f.max_ctx * f.head_dim * 2;
+  c->lin_bytes = (int64_t)f.max_batch * f.lin_heads * f.d_v * f.d_k * 4;
+  c->latent_bytes = (int64_t)f.max_batch * f.max_ctx * (f.kv_rank + f.rope_dim) * 2;
+  return MK_OK;
+}
+
+// The slot and row offset that a weight descriptor fills.
+mk_status resolve(mk_ctx *c, const mk_weight_desc &w, Slot **slot, int64_t *row_off, int64_t *rows, int64_t *cols,
+                  uint32_t **have) {
+  const mk_config &f = c->cfg;
+  const int H = f.hidden;
+  if (w.expert != -1) return fail(MK_E_UNSUPPORTED, "expert tensors are not built yet");
+  *row_off = 0;
+  if (w.layer == -1) {
+    *have = &c->global_have;
+    if (f.vocab <= 0) return fail(MK_E_ARG, "global tensor kind %d in a slice configuration", w.kind);
+    switch (w.kind) {
+      case MK_W_EMBED: *slot = &c->embed; *rows = f.vocab; *cols = H; return MK_OK;
+      case MK_W_FINAL_NORM: *slot = &c->final_norm; *rows = 1; *cols = H; return MK_OK;
+      case MK_W_LM_HEAD: *slot = &c->lm_head; *rows = f.vocab; *cols = H; return MK_OK;
+      default: return fail(MK_E_ARG, "kind %d is not a global tensor", w.kind);
+    }
+  }
+  if (w.layer < 0 || w.layer >= f.n_layers) return fail(MK_E_ARG, "layer %d out of range", w.layer);
+  LayerSlots &s = c->L[w.layer];
+  *have = &s.have;
+  const int m = f.mixer[w.layer];
+  const bool lin = m == MK_MIXER_GDN || m == MK_MIXER_KDA;
+  switch (w.kind) {
+    case MK_W_ATTN_NORM: *slot = &s.attn_norm; *rows = 1; *cols = H; return MK_OK;
+    case MK_W_FFN_NORM: *slot = &s.ffn_norm; *rows = 1; *cols = H; return MK_OK;
+    case MK_W_Q:
+      *slot = &s.mix_in; *row_off = s.q_off; *cols = H;
+      *rows = lin ? (int64_t)f.lin_heads * f.d_k : (int64_t)f.n_q_heads * f.head_dim;
+      return MK_OK;
+    case MK_W_K:
+      *slot = &s.mix_in; *row_off = s.k_off; *cols = H;
+      *rows = lin ? (int64_t)f.lin_heads * f.d_k : (int64_t)f.n_kv_heads * f.head_dim;
+      return MK_OK;
+    case MK_W_V:
+      *slot = &s.mix_in; *row_off = s.v_off; *cols = H;
+      *rows = lin ? (int64_t)f.lin_heads * f.d_v : (int64_t)f.n_kv_heads * f.head_dim;
+      return MK_OK;
+    case MK_W_A:
+      if (!lin) break;
+      *slot = &s.mix_in; *row_off = s.a_off; *cols = H;
+      *rows = m == MK_MIXER_KDA ? (int64_t)f.lin_heads * f.d_k : f.lin_heads;
+      return MK_OK;
+    case MK_W_B:
+      if (!lin) break;
+      *slot = &s.mix_in; *row_off = s.b_off; *cols = H; *rows = f.lin_heads;
+      return MK_OK;
+    case MK_W_O: *slot = &s.wo; *rows = H; *cols = s.wo.K; return MK_OK;
+    case MK_W_GATE: *slot = &s.gu; *rows = f.ffn; *cols = H; return MK_OK;
+    case MK_W_UP: *slot = &s.gu; *row_off = f.ffn; *rows = f.ffn; *cols = H; return MK_OK;
+    case MK_W_DOWN: *slot = &s.wd; *rows = H; *cols = f.ffn; return MK_OK;
+    default: break;
+  }
+  return fail(MK_E_ARG, "layer %d: weight kind %d does not apply to this layer", w.layer, w.kind);
+}
+
+void fill_args(mk_ctx *c, StepArgs &a, int R, int verify, const mk_step_io *io) {
+  const mk_config &f = c->cfg;
+  memset(&a, 0, sizeof(a));
+  const Schedule &sc = c->sched[R];
+  a.phases = reinterpret_cast<const Phase *>(c->scratch + c->o_phases[R]);
+  a.n_phases = (int)sc.phases.size();
+  a.n_barriers = a.n_phases - 1;
+  a.epoch = c->epoch;
+  a.R = R;
+  a.verify = verify;
+  a.phase_begin = 0;
+  a.phase_end = a.n_phases;
+  a.wbuf = c->wbuf;
+  a.bar = reinterpret_cast<uint32_t *>(c->scratch + c->o_bar);
+  a.fin = reinterpret_cast<uint32_t *>(c->scratch + c->o_fin);
+  a.status = reinterpret_cast<int32_t *>(c->scratch + c->o_status);
+  a.x = reinterpret_cast<float *>(c->scratch + c->o_x);
+  a.ss = reinterpret_cast<float *>(c->scratch + c->o_ss);
+  a.part[0] = reinterpret_cast<float *>(c->scratch + c->o_part[0]);
+  a.part[1] = reinterpret_cast<float *>(c->scratch + c->o_part[1]);
+  a.mix = reinterpret_cast<float *>(c->scratch + c->o_mix);
+  a.attn = reinterpret_cast<float *>(c->scratch + c->o_attn);
+  a.cand = reinterpret_cast<float *>(c->scratch + c->o_cand);
+  a.rope = reinterpret_cast<const float *>(c->scratch + c->o_rope);
+  a.snap = reinterpret_cast<float *>(c->scratch + c->o_snap);
+  void **ptrs = reinterpret_cast<void **>(c->scratch + c->o_ptrs);
+  a.kc = ptrs;
+  a.vc = ptrs + MK_MAX_LAYERS;
+  a.ls = ptrs + 2 * MK_MAX_LAYERS;
+  a.lsl = ptrs + 3 * MK_MAX_LAYERS;
+  a.tokens = io->tokens;
+  a.hidden_in = io->hidden_in;
+  const int nseq = verify ? 1 : R;
+  for (int b = 0; b < nseq; ++b) a.pos[b] = io->positions[b];
+  a.logits = io->logits;
+  a.hidden_out = io->hidden_out;
+  a.argmax = io->argmax;
+  a.H = f.hidden;
+  a.V = f.vocab;
+  a.max_ctx = f.max_ctx;
+  a.mix_stride = c->mix_stride;
+  a.nq = f.n_q_heads;
+  a.nkv = f.n_kv_heads;
+  a.hd = f.head_dim;
+  a.lin_heads = f.lin_heads;
+  a.dk = f.d_k;
+  a.dv = f.d_v;
+  a.n_lin = c->n_lin;
+  a.eps = f.eps;
+  a.timeout_ticks = 200000000;  // 2 s at 100 MHz
+}
+
+mk_status check_step(mk_ctx *c, const mk_step_io *io, int R, int nseq, int nrow) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  if (c->device < 0) return fail(MK_E_UNSUPPORTED, "host-only context");
+  if (!c->bound) return fail(MK_E_STATE, "buffers are not bound");
+  if (!io) return fail(MK_E_ARG, "io is NULL");
+  const mk_config &f = c->cfg;
+  if (c->global_have != c->global_need) return fail(MK_E_STATE, "global weights missing (mask %x of %x)", c->global_have, c->global_need);
+  for (int l = 0; l < f.n_layers; ++l)
+    if (c->L[l].have != c->L[l].need) return fail(MK_E_STATE, "layer %d weights missing (mask %x of %x)", l, c->L[l].have, c->L[l].need);
+  if (!io->positions) return fail(MK_E_ARG, "positions is NULL");
+  if (f.vocab > 0) {
+    if (!io->tokens || !io->logits) return fail(MK_E_ARG, "tokens and logits are required");
+  } else {
+    if (!io->hidden_in || !io->hidden_out) return fail(MK_E_ARG, "hidden_in and hidden_out are required");
+  }
+  for (int b = 0; b < nseq; ++b) {
+    const int p = io->positions[b];
+    if (p < 0 || (int64_t)p + nrow > f.max_ctx)
+      return fail(MK_E_CAPACITY, "position %d + %d rows exceeds max_ctx %d", p, nrow, f.max_ctx);
+  }
+  if (c->sched[R].phases.empty()) return fail(MK_E_CAPACITY, "no schedule for %d rows", R);
+  return MK_OK;
+}
+
+mk_status reset_counters(mk_ctx *c, hipStream_t st) {
+  HIP_TRY(hipMemsetAsync(c->scratch + c->o_status, 0, 256, st));
+  HIP_TRY(hipMemsetAsync(c->scratch + c->o_bar, 0, 9 * 128, st));
+  HIP_TRY(hipMemsetAsync(c->scratch + c->o_fin, 0, ((size_t)c->n_resid * (c->cfg.hidden / kTileRows) + c->cfg.vocab / kTileRows) * 4, st));
+  c->epoch = 0;
+  c->needs_reset = false;
+  return MK_OK;
+}
+
+mk_status launch_step(mk_ctx *c, StepArgs &a, hipStream_t st) {
+  void *args[] = {&a};
+  HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void *>(mk_step_kernel), dim3(c->G), dim3(kThreads), args,
+                                     kLdsBytes, st));
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mk_last_error(void) { return g_err.c_str(); }
+
+mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
+  if (!out) return fail(MK_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (mk_status st = validate(cfg)) return st;
+  mk_ctx *c = new mk_ctx();
+  c->cfg = *cfg;
+  c->device = hip_device;
+  c->max_rows = cfg->vocab > 0 ? kMaxRows : cfg->max_batch;
+  if (hip_device >= 0) {
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, hip_device);
+    if (e != hipSuccess) { delete c; return fail(MK_E_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e)); }
+    if (std::string(prop.gcnArchName).find("gfx950") == std::string::npos) {
+      delete c;
+      return fail(MK_E_UNSUPPORTED, "device %d is %s; this build targets gfx950", hip_device, prop.gcnArchName);
+    }
+    c->G = prop.multiProcessorCount;
+  } else {
+    c->G = 256;  // host-only context: MI355X compute unit count
+  }
+  memset(&c->bufs, 0, sizeof(c->bufs));
+  mk_status st = layout(c);
+  for (int r = 1; st == MK_OK && r <= kMaxRows; ++r) {
+    if (r > c->max_rows) break;
+    st = build_schedule(c, r, c->sched[r]);
+  }
+  if (st == MK_OK) st = scratch_layout(c);
+  if (st != MK_OK) { delete c; return st; }
+  if (hip_device >= 0) {
+    hipError_t e = hipSetDevice(hip_device);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(mk_step_kernel), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) { delete c; return fail(MK_E_HIP, "kernel setup: %s", hipGetErrorString(e)); }
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(mk_step_kernel), kThreads, kLdsBytes);
+    if (e != hipSuccess || nb < 1) {
+      delete c;
+      return fail(MK_E_HIP, "step kernel cannot be resident (%d per CU): %s", nb, hipGetErrorString(e));
+    }
+  }
+  *out = c;
+  return MK_OK;
+}
+
+mk_status mk_query_sizes(const mk_ctx *c, mk_sizes *out) {
+  if (!c || !out) return fail(MK_E_ARG, "NULL argument");
+  out->packed_weights = (uint64_t)c->packed_bytes;
+  out->scratch = (uint64_t)c->scratch_bytes;
+  out->kv_cache_per_layer = (uint64_t)c->kv_bytes;
+  out->lin_state_per_layer = (uint64_t)c->lin_bytes;
+  out->latent_per_layer = (uint64_t)c->latent_bytes;
+  out->n_phases = (int32_t)c->sched[1].phases.size();
+  out->n_workgroups = c->G;
+  return MK_OK;
+}
+
+mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
+  if (!c || !b) return fail(MK_E_ARG, "NULL argument");
+  if (c->device < 0) return fail(MK_E_UNSUPPORTED, "host-only context");
+  const mk_config &f = c->cfg;
+  if (!b->packed_weights || !b->scratch) return fail(MK_E_ARG, "packed_weights and scratch are required");
+  if (((uintptr_t)b->packed_weights | (uintptr_t)b->scratch) & 255) return fail(MK_E_ARG, "buffers must be 256-byte aligned");
+  for (int l = 0; l < f.n_layers; ++l) {
+    const int m = f.mixer[l];
+    if (m == MK_MIXER_GQA && (!b->k_cache[l] || !b->v_cache[l])) return fail(MK_E_ARG, "layer %d: K/V cache missing", l);
+    if ((m == MK_MIXER_GDN || m == MK_MIXER_KDA) && !b->lin_state[l]) return fail(MK_E_ARG, "layer %d: state missing", l);
+  }
+  HIP_TRY(hipSetDevice(c->device));
+  c->bufs = *b;
+  c->wbuf = static_cast<uint8_t *>(b->packed_weights);
+  c->scratch = static_cast<uint8_t *>(b->scratch);
+  HIP_TRY(hipMemset(c->wbuf, 0, (size_t)c->packed_bytes));  // padding rows of fused matrices are zero
+  HIP_TRY(hipMemset(c->scratch, 0, (size_t)c->scratch_bytes));
+  // per-layer state pointers
+  std::vector<void *> ptrs(4 * MK_MAX_LAYERS, nullptr);
+  for (int l = 0; l < f.n_layers; ++l) {
+    ptrs[l] = b->k_cache[l];
+    ptrs[MK_MAX_LAYERS + l] = b->v_cache[l];
+    ptrs[2 * MK_MAX_LAYERS + l] = b->lin_state[l];
+    if (c->lin_index[l] >= 0) ptrs[3 * MK_MAX_LAYERS + c->lin_index[l]] = b->lin_state[l];
+  }
+  HIP_TRY(hipMemcpy(c->scratch + c->o_ptrs, ptrs.data(), ptrs.size() * 8, hipMemcpyHostToDevice));
+  // rotary table: angle p * theta^(-2i/d) in double, cosine and sine rounded to fp32
+  if (f.n_q_heads > 0) {
+    const int half = f.head_dim / 2;
+    std::vector<float> rope((size_t)f.max_ctx * half * 2);
+    for (int p = 0; p < f.max_ctx; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * std::pow((double)f.rope_theta, -2.0 * i / (double)f.head_dim);
+        rope[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+        rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    HIP_TRY(hipMemcpy(c->scratch + c->o_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
+  }
+  for (int r = 1; r <= kMaxRows; ++r) {
+    const Schedule &s = c->sched[r];
+    if (s.phases.empty()) continue;
+    HIP_TRY(hipMemcpy(c->scratch + c->o_phases[r], s.phases.data(), s.phases.size() * sizeof(Phase), hipMemcpyHostToDevice));
+  }
+  c->epoch = 0;
+  c->bound = true;
+  c->global_have = 0;
+  for (auto &s : c->L) s.have = 0;
+  return MK_OK;
+}
+
+mk_status mk_load_weights(mk_ctx *c, const mk_weight_desc *w, int n, void *stream) {
+  if (!c || (!w && n > 0) || n < 0) return fail(MK_E_ARG, "bad arguments");
+  if (c->device < 0) return fail(MK_E_UNSUPPORTED, "host-only context");
+  if (!c->bound) return fail(MK_E_STATE, "buffers are not bound");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // validate all first (a rejected call enqueues nothing)
+  for (int i = 0; i < n; ++i) {
+    Slot *slot;
+    int64_t ro, rows, cols;
+    uint32_t *have;
+    if (mk_status s = resolve(c, w[i], &slot, &ro, &rows, &cols, &have)) return s;
+    if (w[i].dtype != MK_DT_BF16) return fail(MK_E_UNSUPPORTED, "tensor %d: only bf16 dense weights are built yet", i);
+    if (w[i].rows != rows || w[i].cols != cols)
+      return fail(MK_E_SHAPE, "tensor %d (layer %d kind %d): shape %lldx%lld, expected %lldx%lld", i, w[i].layer, w[i].kind,
+                  (long long)w[i].rows, (long long)w[i].cols, (long long)rows, (long long)cols);
+    if (!w[i].data || ((uintptr_t)w[i].data & 15)) return fail(MK_E_ARG, "tensor %d: data must be 16-byte aligned", i);
+  }
+  HIP_TRY(hipSetDevice(c->device));
+  for (int i = 0; i < n; ++i) {
+    Slot *slot;
+    int64_t ro, rows, cols;
+    uint32_t *have;
+    resolve(c, w[i], &slot, &ro, &rows, &cols, &have);
+    if (!slot->packed) {
+      HIP_TRY(hipMemcpyAsync(c->wbuf + slot->off, w[i].data, (size_t)rows * cols * 2, hipMemcpyDeviceToDevice, st));
+    } else {
+      const int64_t KF = cols / kFragK;
+      const int64_t total = ((rows + 15) / 16) * KF * 64;
+      const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+      hipLaunchKernelGGL(mk_repack_bf16, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(w[i].data), rows, cols,
+                         reinterpret_cast<uint4 *>(c->wbuf + slot->off), ro, KF);
+      HIP_TRY(hipGetLastError());
+    }
+    *have |= kind_bit(w[i].kind);
+  }
+  return MK_OK;
+}
+
+mk_status mk_decode_step(mk_ctx *c, const mk_step_io *io, int batch, void *stream) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  if (batch < 1 || batch > c->cfg.max_batch) return fail(MK_E_CAPACITY, "batch %d out of [1, %d]", batch, c->cfg.max_batch);
+  if (mk_status s = check_step(c, io, batch, batch, 1)) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipSetDevice(c->device));
+  if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
+  ++c->epoch;
+  StepArgs a;
+  fill_args(c, a, batch, 0, io);
+  return launch_step(c, a, st);
+}
+
+mk_status mk_verify_step(mk_ctx *c, const mk_step_io *io, int32_t *d_accepted, int32_t *d_bonus, void *stream) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  if (c->cfg.vocab <= 0) return fail(MK_E_UNSUPPORTED, "verify needs a vocabulary (logits) configuration");
+  if (!d_accepted || !d_bonus) return fail(MK_E_ARG, "accepted and bonus outputs are required");
+  if (mk_status s = check_step(c, io, kMaxRows, 1, kMaxRows)) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipSetDevice(c->device));
+  if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
+  ++c->epoch;
+  StepArgs a;
+  fill_args(c, a, kMaxRows, 1, io);
+  a.accepted = d_accepted;
+  a.bonus = d_bonus;
+  return launch_step(c, a, st);
+}
+
+mk_status mk_decode_step_perop(mk_ctx *c, const mk_step_io *io, int batch, int use_graph, void *stream) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  if (batch < 1 || batch > c->cfg.max_batch) return fail(MK_E_CAPACITY, "batch %d out of [1, %d]", batch, c->cfg.max_batch);
+  if (mk_status s = check_step(c, io, batch, batch, 1)) return s;
+  if (use_graph) return fail(MK_E_UNSUPPORTED, "graph capture of the per-op baseline is not built yet");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipSetDevice(c->device));
+  if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
+  ++c->epoch;
+  StepArgs a;
+  fill_args(c, a, batch, 0, io);
+  const int n = a.n_phases;
+  for (int p = 0; p < n; ++p) {
+    a.phase_begin = p;
+    a.phase_end = p + 1;
+    a.barrier_base = p;
+    hipLaunchKernelGGL(mk_step_kernel, dim3(c->G), dim3(kThreads), kLdsBytes, st, a);
+    HIP_TRY(hipGetLastError());
+  }
+  return MK_OK;
+}
+
+mk_status mk_read_device_status(mk_ctx *c, int32_t *status, int32_t *phase) {
+  if (!c || !status || !phase) return fail(MK_E_ARG, "NULL argument");
+  if (c->device < 0 || !c->bound) return fail(MK_E_STATE, "no bound device context");
+  int32_t s[3] = {0, 0, 0};
+  HIP_TRY(hipSetDevice(c->device));
+  HIP_TRY(hipMemcpy(s, c->scratch + c->o_status, sizeof(s), hipMemcpyDeviceToHost));
+  *status = s[0];
+  *phase = s[0] ? s[1] : -1;
+  if (s[0] != 0) c->needs_reset = true;
+  return MK_OK;
+}
+
+void mk_destroy(mk_ctx *c) {
+  if (!c) return;
+  for (auto &g : c->graph)
+    if (g) hipGraphExecDestroy(g);
+  delete c;
+}
+
+// Host-logic introspection for tests (no device needed): the phase table for a row count.
+int mk_debug_phase_count(const mk_ctx *c, int rows) {
+  if (!c || rows < 1 || rows > kMaxRows) return -1;
+  return (int)c->sched[rows].phases.size();
+}
+
+int mk_debug_phase(const mk_ctx *c, int rows, int i, int32_t *out16) {
+  if (!c || rows < 1 || rows > kMaxRows || i < 0 || i >= (int)c->sched[rows].phases.size() || !out16) return -1;
+  const Phase &p = c->sched[rows].phases[(size_t)i];
+  const int32_t v[16] = {p.type, p.layer, p.N, p.K, p.T, p.KF, p.S, p.nf, p.act, p.out, p.src_S, p.src_N, p.n_chunks, p.chunk,
+                         p.dst_part, p.cnt_off};
+  memcpy(out16, v, sizeof(v));
+  return 0;
+}
+
+}  // extern "C"

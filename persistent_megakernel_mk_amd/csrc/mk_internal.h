@@ -1,0 +1,107 @@
+// Shared host/device definitions of the megakernel: the phase table the host builds and the kernel
+// interprets, and the argument block of one step launch. Internal to libmk.so.
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int kWaves = 8;                 // compute waves per workgroup
+constexpr int kThreads = kWaves * 64;     // threads per workgroup
+constexpr int kTileRows = 16;             // weight rows per MFMA tile
+constexpr int kFragK = 32;                // reduction columns per 1 KiB weight fragment
+constexpr int kLdsBytes = 160 * 1024 - 512;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU, minus static)
+constexpr int kActLdsBudget = 96 * 1024;  // activation fragments of one k-split
+constexpr int kMaxRows = 8;               // rows per step (batch or verify block)
+constexpr int kAttnMaxChunk = 128;        // positions per split-KV chunk
+constexpr int kMaxUnits = 512;            // product units (tile x k-split) per workgroup and phase
+constexpr int kAttnMaxQ = 64;             // queries per split-KV unit (query heads per kv head x rows)
+
+enum PhaseType : int32_t {
+  PH_EMBED = 1,      // residual x <- embedding rows (or hidden_in); per-tile sums of squares
+  PH_GEMV = 2,       // weight-streaming matrix-vector product (MFMA, bf16 weights, fp32 accumulation)
+  PH_DELTA = 3,      // gated delta rule state update + readout (scalar or per-channel gate)
+  PH_ATTN = 4,       // split-KV grouped-query attention partials (+ RoPE and K/V append)
+  PH_MERGE = 5,      // log-sum-exp merge of the split-KV partials
+  PH_FINAL = 6,      // argmax over LM-head candidates; verify accept + state commit
+  PH_HIDDEN_OUT = 7  // slice configs: x -> hidden_out
+};
+
+enum ActKind : int32_t {
+  ACT_NORM = 0,   // y = x * rstd * gain    (rstd from per-tile sums of squares)
+  ACT_PART = 1,   // y = sum over S_src partials of the previous product
+  ACT_SWIGLU = 2, // y = silu(sum gate partials) * (sum up partials); up rows follow gate rows
+  ACT_MIX = 3     // y = mixer output vector
+};
+
+enum OutKind : int32_t {
+  OUT_PART = 0,   // partial sums per k-split -> part[dst]
+  OUT_RESID = 1,  // partial sums, then the last contributor of each tile adds them into x
+  OUT_LOGITS = 2  // final values (one k-split) -> logits, plus per-workgroup argmax candidates
+};
+
+struct Phase {
+  int32_t type;
+  int32_t layer;
+  // ---- GEMV ----
+  int64_t w_off;     // byte offset of the packed matrix in the weight buffer
+  int64_t gain_off;  // byte offset of the bf16 RMSNorm gain (ACT_NORM)
+  int32_t N, K;      // rows, columns
+  int32_t T, KF;     // 16-row tiles, 32-column fragments
+  int32_t S, nf;     // k-splits, fragments per split (nf = KF / S, a multiple of kWaves)
+  int32_t act, out;
+  int32_t src_part, src_S, src_N, src_off;  // activation partials: buffer, splits, row stride, row offset
+  int32_t dst_part;  // partial buffer written
+  int32_t cnt_off;   // finalizer counters (OUT_RESID)
+  // ---- mixers ----
+  int32_t lin_idx;   // index among linear-attention layers (state snapshots)
+  int32_t per_channel_gate;  // 1: Kimi delta attention (gate per key channel)
+  int32_t n_chunks, chunk;   // split-KV geometry
+  int32_t q_off, k_off, v_off, a_off, b_off;  // row offsets inside the fused projection output
+  int32_t pad[3];
+};
+
+struct StepArgs {
+  const Phase *phases;
+  int32_t n_phases;
+  int32_t n_barriers;  // grid barriers per step
+  uint32_t epoch;      // 1-based step counter of this context (targets of monotone counters)
+  int32_t R;           // rows in this step: batch, or 8 for verify
+  int32_t verify;
+  int32_t phase_begin, phase_end;  // phases run by this launch (all, or one for the per-op baseline)
+  int32_t barrier_base;            // barriers completed before phase_begin within this step
+  const uint8_t *wbuf;
+  // scratch regions
+  uint32_t *bar;       // 9 counters, 128 B apart (8 groups + top)
+  uint32_t *fin;       // finalizer counters
+  int32_t *status;     // [0] status, [1] phase, [2] abort flag
+  float *x;            // residual [R][H]
+  float *ss;           // [R][H/16] per-tile sums of squares of x
+  float *part[2];      // partial sums [S][R][N]
+  float *mix;          // mixer outputs [R][M]
+  float *attn;         // split-KV partials [R][nq][n_chunks][hd + 2]
+  float *cand;         // argmax candidates [G][R][2]
+  const float *rope;   // [max_ctx][hd/2][2] cos, sin
+  float *snap;         // verify snapshots [lin layers][8][heads][d_v][d_k]
+  void *const *kc;     // per layer K cache pointers
+  void *const *vc;
+  void *const *ls;     // per layer linear states
+  void *const *lsl;    // per linear-attention index: state pointers (verify commit)
+  // io
+  const int32_t *tokens;
+  const float *hidden_in;
+  int32_t pos[kMaxRows];  // position of each sequence's new token (verify: of the anchor)
+  float *logits;
+  float *hidden_out;
+  int32_t *argmax;
+  int32_t *accepted;
+  int32_t *bonus;
+  // config scalars
+  int32_t H, V, max_ctx, mix_stride;
+  int32_t nq, nkv, hd;
+  int32_t lin_heads, dk, dv, n_lin;
+  int32_t part_stride;  // floats per partial buffer
+  float eps;
+  int64_t timeout_ticks;  // bound of every in-kernel wait, in s_memrealtime ticks (100 MHz)
+};
+
+}  // namespace mk

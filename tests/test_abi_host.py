@@ -1,0 +1,90 @@
+"""The C ABI library without a GPU: it loads, exports every entry point include/mk.h declares, validates
+configurations, and builds the step schedule (host-only contexts, hip_device = -1)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mk.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:mk_status|void|const char \*|int)\s*\*?\s*(mk_[a-z_]+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def mkmod():
+    from persistent_megakernel_mk_amd import mk
+
+    return mk
+
+
+def test_library_exports_every_declared_symbol(mkmod):
+    lib = mkmod.load()
+    names = declared_functions()
+    assert "mk_decode_step" in names and "mk_verify_step" in names and "mk_load_weights" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts_match_header(mkmod):
+    # sizes implied by the header's field lists (LP64)
+    assert ctypes.sizeof(mkmod.Config) == 4 * (3 + 2 * 128 + 1 + 3 + 3 + 5 + 5 + 2) + 8
+    assert ctypes.sizeof(mkmod.WeightDesc) == 16 + 16 + 16 + 8
+    assert ctypes.sizeof(mkmod.StepIO) == 8 * 8
+    assert ctypes.sizeof(mkmod.Buffers) == 8 * (2 + 4 * 128)
+
+
+def test_invalid_configs_are_rejected(mkmod, synth):
+    from dataclasses import replace
+
+    cfg = synth.CONFIGS["c1s"]
+    for bad, status in [(replace(cfg, hidden=1000), 3), (replace(cfg, n_layers=0, mixers=(), ffns=()), 1),
+                        (replace(cfg, head_dim=96), 3), (replace(cfg, n_kv_heads=4), 1)]:
+        with pytest.raises(mkmod.MKError) as ei:
+            mkmod.HostContext(bad)
+        assert ei.value.status == status
+    with pytest.raises(mkmod.MKError):
+        mkmod.HostContext(cfg, max_batch=9)
+
+
+def test_schedule_layer_pattern_and_phase_counts(mkmod, synth):
+    cfg = synth.CONFIGS["c1"]
+    h = mkmod.HostContext(cfg, max_batch=8)
+    ph = h.phases(1)
+    types = [p[0] for p in ph]
+    # embed; per GDN layer: product, delta rule, product, product, product; per GQA layer one more
+    # (attention partials + merge); LM head; final
+    n_gqa = sum(1 for m in cfg.mixers if m == "gqa")
+    assert n_gqa == 16 and cfg.mixers[3] == "gqa" and cfg.mixers[0] == "gdn"
+    assert len(ph) == 1 + 5 * 64 + n_gqa + 2 == h.sizes.n_phases
+    assert types[0] == 1 and types[-1] == 6 and types[-2] == 2
+    assert types.count(3) == 48 and types.count(4) == 16 and types.count(5) == 16
+    # the 4th layer (index 3) uses attention: embed + 3 * 5 phases precede it
+    assert types[16] == 2 and types[17] == 4 and types[18] == 5
+
+
+def test_split_choice_respects_lds_and_waves(mkmod, synth):
+    cfg = synth.CONFIGS["c1"]
+    h = mkmod.HostContext(cfg, max_batch=8)
+    for rows in range(1, 9):
+        for p in h.phases(rows):
+            if p[0] != 2:
+                continue
+            N, K, T, KF, S, nf = p[2], p[3], p[4], p[5], p[6], p[7]
+            assert T * 16 == N and KF * 32 == K
+            assert S >= 1 and KF == S * nf and nf % 8 == 0
+            assert nf * 128 * rows <= 96 * 1024  # activation fragments of one split fit the LDS budget
+
+
+def test_sizes(mkmod, synth):
+    cfg = synth.CONFIGS["c1"]
+    h = mkmod.HostContext(cfg, max_batch=1)
+    s = h.sizes
+    assert s.kv_cache_per_layer == 1 * 4 * cfg.max_ctx * 128 * 2
+    assert s.lin_state_per_layer == 16 * 128 * 128 * 4
+    # packed weights hold every matrix once (plus 256-byte alignment and the fused a/b row padding)
+    params = sum(sp.numel for sp in synth.weight_specs(cfg))
+    assert params * 2 <= s.packed_weights <= params * 2 + 64 * 64 * 1024
