@@ -1,0 +1,69 @@
+"""Byte accounting of a decode step: the algorithmic bytes the step must move, and the byte formulas
+the pages use for the Kimi K3 expert formats.
+
+A decode step at small batch streams every weight it touches about once, at roughly one FLOP per byte
+(page "Kimi K3's TPU megakernel: 92 layers in one Pallas call, and what 709 tokens a second measures",
+section "Why one user at a time is a bandwidth problem"); its floor is bytes over bandwidth (same page,
+section "The bandwidth arithmetic"). Algorithmic bytes count each touched weight once, the K/V (or
+latent) cache rows read and the new rows written, the linear-attention state read and written, the
+embedding rows gathered and the logits (or hidden states) written. Over-fetch, padding and reductions
+are not counted.
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def mxfp4_bytes(n_params: int) -> float:
+    """MXFP4: 4-bit E2M1 values plus one 8-bit E8M0 scale per 32 values = 4.25 bits per value."""
+    return n_params * 4.25 / 8
+
+
+def fp8_rowscaled_bytes(rows: int, cols: int, rows_per_scale: int = 256) -> float:
+    """FP8 E4M3 values with one bf16 scale per `rows_per_scale` rows of each column."""
+    return rows * cols * (1 + 2 / rows_per_scale)
+
+
+def kimi_expert_bytes(hidden: int = 7168, expert_ffn: int = 1536) -> Dict[str, float]:
+    """One routed expert (gate, up, down of hidden x expert_ffn), stored as the pages describe:
+    all three projections in MXFP4, or gate/up re-encoded to FP8 with a bf16 scale per 256 rows and down
+    kept in MXFP4 (page "Kimi K3's TPU megakernel ...", section "How it maps onto a TPU v7")."""
+    n = hidden * expert_ffn
+    return {"mxfp4": mxfp4_bytes(3 * n),
+            "fp8_gate_up_mxfp4_down": 2 * fp8_rowscaled_bytes(hidden, expert_ffn) + mxfp4_bytes(n)}
+
+
+def roofline_floor_ms(bytes_per_token: float, devices: int, gbs_per_device: float) -> float:
+    return bytes_per_token / (devices * gbs_per_device * 1e9) * 1e3
+
+
+def step_bytes(cfg, batch: int, position: int, rows: int = 1) -> Dict[str, float]:
+    """Algorithmic bytes of one decode step (rows = 1) or verify block (rows = 8, batch = 1) of a dense
+    bf16 configuration. `position` is the position of the (first) new token, so position cached rows are
+    read per sequence and kv head."""
+    from persistent_megakernel_mk_amd import synth
+
+    w = 0
+    for s in synth.weight_specs(cfg):
+        if s.name == "embed":
+            continue  # only the gathered rows are read
+        w += s.numel * (2 if s.kind == "bf16" else 0)
+    seqs = batch
+    toks = batch * rows
+    emb = toks * cfg.hidden * 2 if cfg.vocab else toks * cfg.hidden * 4
+    kv = lin = 0
+    for l in range(cfg.n_layers):
+        m = cfg.mixers[l]
+        if m == "gqa":
+            row = cfg.n_kv_heads * cfg.head_dim * 2  # one position of K (or V), bf16
+            kv += seqs * 2 * (position * row) + toks * 2 * row
+        elif m in ("gdn", "kda"):
+            st = cfg.lin_heads * cfg.d_v * cfg.d_k * 4
+            lin += seqs * 2 * st
+            if rows > 1:
+                lin += rows * st  # one snapshot per verify row
+    out = toks * cfg.vocab * 4 if cfg.vocab else toks * cfg.hidden * 4
+    total = w + emb + kv + lin + out
+    return {"weights": w, "embed": emb, "kv": kv, "lin_state": lin, "out": out, "total": total}

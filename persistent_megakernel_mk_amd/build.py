@@ -37,6 +37,7 @@ def build_all(verbose: bool = False) -> None:
     from persistent_megakernel_mk_amd import synth
 
     synth.build_host_lib(force=True)
+    synth.build_gpu_lib()
     build_lib(verbose)
 
 

@@ -33,6 +33,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmksynth.so")
+_GPU_LIB_PATH = os.path.join(_HERE, "libmksynth_gpu.so")
 
 # ----------------------------------------------------------------------------------------------
 # configurations
@@ -246,6 +247,19 @@ def build_host_lib(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def build_gpu_lib() -> str:
+    """Compile the device generator (hipcc, gfx950)."""
+    import subprocess
+
+    src = os.path.join(_HERE, "synth_gpu.hip")
+    tmp = _GPU_LIB_PATH + ".tmp"
+    subprocess.check_call(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "-fPIC", "-shared", "-ffp-contract=off",
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", tmp, src],
+                          stderr=subprocess.DEVNULL)
+    os.replace(tmp, _GPU_LIB_PATH)
+    return _GPU_LIB_PATH
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
@@ -368,6 +382,56 @@ def make_inputs(cfg: ModelConfig, step: int = 0) -> Dict[str, np.ndarray]:
             out[s.name] = uniform_int(cfg.seed, tid, s.numel, cfg.vocab).reshape(s.shape)
         else:
             out[s.name] = normal_f32(cfg.seed, tid, s.numel, s.sigma).reshape(s.shape)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# device generator (same values, generated in device memory; libmksynth_gpu.so)
+# ----------------------------------------------------------------------------------------------
+
+_gpu_lib: Optional[ctypes.CDLL] = None
+
+
+def gpu_lib() -> ctypes.CDLL:
+    global _gpu_lib
+    if _gpu_lib is None:
+        if not os.path.exists(_GPU_LIB_PATH):
+            raise RuntimeError(f"{_GPU_LIB_PATH} is not built (persistent_megakernel_mk_amd/build.py)")
+        L = ctypes.CDLL(_GPU_LIB_PATH)
+        u64, i64, f32, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+        L.synth_gpu_normal_bf16.argtypes = [u64, u64, i64, f32, f32, i64, i64, i64, vp, vp]
+        L.synth_gpu_normal_bf16.restype = ctypes.c_int
+        L.synth_gpu_normal_f32.argtypes = [u64, u64, i64, f32, f32, vp, vp]
+        L.synth_gpu_normal_f32.restype = ctypes.c_int
+        _gpu_lib = L
+    return _gpu_lib
+
+
+def generate_gpu(spec: TensorSpec, seed: int, device="cuda"):
+    """Materialise one bf16/f32 tensor directly in device memory (torch), bit-identical to generate()."""
+    import torch
+
+    key = lib().synth_key(seed, spec.tid)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    if spec.kind == "bf16":
+        out = torch.empty(spec.shape, dtype=torch.bfloat16, device=device)
+        inner = positions = 1
+        valid = -1
+        if spec.valid_positions >= 0:
+            if spec.name.endswith("latent"):
+                inner, positions = spec.shape[2], spec.shape[1]
+            else:
+                inner, positions = spec.shape[3], spec.shape[2]
+            valid = spec.valid_positions
+        rc = gpu_lib().synth_gpu_normal_bf16(key, 0, spec.numel, spec.sigma, spec.mean, inner, positions, valid,
+                                             out.data_ptr(), stream)
+    elif spec.kind == "f32":
+        out = torch.empty(spec.shape, dtype=torch.float32, device=device)
+        rc = gpu_lib().synth_gpu_normal_f32(key, 0, spec.numel, spec.sigma, spec.mean, out.data_ptr(), stream)
+    else:
+        raise ValueError(f"device generation of {spec.kind} is not provided")
+    if rc != 0:
+        raise RuntimeError(f"device generator launch failed ({rc})")
     return out
 
 
