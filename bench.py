@@ -88,6 +88,45 @@ def time_steps(m, cfg, batch, steps, warmup, perop=False):
             "p90_ms": per[int(0.9 * (steps - 1))], "wall_ms": wall}
 
 
+PHASE_NAMES = {1: "embed", 2: "product", 3: "delta-rule", 4: "attention", 5: "merge", 6: "final", 7: "hidden-out"}
+
+
+def trace_step(m, cfg, batch):
+    """One traced step: per phase, the span from the first workgroup's start to the last one's end of
+    work, and the gap to the next phase (grid barrier). Summed by phase kind (products by shape)."""
+    import numpy as np
+    import torch
+
+    from persistent_megakernel_mk_amd import synth
+
+    G = m.sizes.n_workgroups
+    ph = m.phases(batch)
+    buf = torch.zeros(len(ph) * G * 2, dtype=torch.int64, device="cuda")
+    m.set_trace(buf)
+    toks = torch.from_numpy(synth.make_inputs(cfg.with_batch(batch))["tokens"]).cuda()
+    for _ in range(2):
+        m.decode([cfg.ctx] * batch, tokens=toks)
+    torch.cuda.synchronize()
+    m.set_trace(None)
+    t = buf.cpu().numpy().reshape(len(ph), G, 2).astype(np.float64) / 100.0  # microseconds
+    start, end = t[:, :, 0], t[:, :, 1]
+    agg = {}
+    total = (end[-1].max() - start[0].min())
+    for i, p in enumerate(ph):
+        key = PHASE_NAMES.get(p[0], str(p[0]))
+        if p[0] == 2:
+            key += f" {p[2]}x{p[3]} S={p[6]}"
+        span = end[i].max() - start[i].min()
+        work_med = float(np.median(end[i] - start[i]))
+        gap = (start[i + 1].min() - end[i].max()) if i + 1 < len(ph) else 0.0
+        a = agg.setdefault(key, [0, 0.0, 0.0, 0.0])
+        a[0] += 1; a[1] += span; a[2] += work_med; a[3] += gap
+    log(f"trace batch {batch}: step {total:.0f} us over {len(ph)} phases")
+    for k, (n, span, wm, gap) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        log(f"  {k:40s} x{n:3d}: span {span:8.0f} us (median wg work {wm:8.0f}), barrier gaps {gap:7.0f} us")
+    return agg
+
+
 def cpu_baseline(cfg_full, layers=4):
     """The CPU oracle, as it stands, on a bounded sample of the same workload: the first `layers` layers
     (one full 3 GDN : 1 GQA group) plus the final norm and LM head, batch 1; the per-token time is
@@ -145,6 +184,7 @@ def main() -> int:
     ap.add_argument("--batches", default="1,8", help="first is the headline; others are reported alongside")
     ap.add_argument("--no-perop", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--trace", action="store_true", help="print a per-phase breakdown of one traced step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the megakernel runs on a single MI355X with no collectives "
@@ -171,6 +211,9 @@ def main() -> int:
         results[b] = r
         log(f"batch {b}: mean {r['mean_ms']:.3f} ms median {r['median_ms']:.3f} ms -> {r['tokens_s']:.1f} tok/s, "
             f"{r['alg_gbs']:.0f} GB/s algorithmic ({100 * r['alg_gbs'] / accounting.HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+    if args.trace:
+        for b in batches:
+            trace_step(m, cfg, b)
     perop = None
     if not args.no_perop:
         r = time_steps(m, cfg, batches[0], max(3, args.steps // 4), 2, perop=True)

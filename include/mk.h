@@ -175,6 +175,12 @@ mk_status mk_read_device_status(mk_ctx *ctx, int32_t *status, int32_t *phase);
 
 void mk_destroy(mk_ctx *ctx);
 
+/* Tracing: when device_buffer is not NULL, every later step records, per phase and workgroup, two
+ * 64-bit timestamps of the GPU's constant 100 MHz clock (phase start, end of the phase's work before
+ * the grid barrier) at [phase][workgroup][2]. bytes must cover the longest schedule
+ * (n_phases * n_workgroups * 16). NULL turns tracing off. Adds one workgroup barrier per phase. */
+mk_status mk_set_trace(mk_ctx *ctx, void *device_buffer, int64_t bytes);
+
 /* Host-logic introspection (works on host-only contexts): number of phases in the schedule for a row
  * count, and 16 integers describing phase i: type, layer, N, K, tiles, fragments, k-splits, fragments
  * per split, activation kind, output kind, source splits, source row stride, split-KV chunks, chunk

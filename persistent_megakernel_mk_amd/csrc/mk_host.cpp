@@ -94,6 +94,7 @@ struct mk_ctx {
   mk_buffers bufs;
   uint32_t epoch = 0;
   bool needs_reset = false;
+  uint64_t *trace = nullptr;  // optional per-phase timestamps (device buffer)
   // per-op baseline graphs
   hipGraphExec_t graph[kMaxRows + 1] = {};
   const void *graph_key[kMaxRows + 1] = {};
@@ -139,19 +140,22 @@ mk_status validate(const mk_config *c) {
   return MK_OK;
 }
 
-// Chooses the k-split count of a product: nf = KF / S a multiple of the wave count, the activation
+// Chooses the k-split count of a product: a power of two dividing the workgroup count (each
+// workgroup works inside one split), nf = KF / S a multiple of the compute-wave count, the activation
 // fragments of one split within the LDS budget, and the fewest fragment-slots on the busiest
-// workgroup (plus a per-unit overhead of a few fragments for the cross-wave reduction).
+// workgroup (plus about one fragment's time per tile for the cross-wave reduction).
 int choose_splits(int T, int KF, int R, int G, int max_S) {
   int best = -1;
   double best_cost = 1e300;
-  for (int S = 1; S <= KF / kWaves; ++S) {
-    if (KF % S || (KF / S) % kWaves || S > max_S) continue;
+  for (int S = 1; S <= KF / kCWaves && S <= G; S *= 2) {
+    if (KF % S || (KF / S) % kCWaves || S > max_S || G % S) continue;
     const int nf = KF / S;
     if ((int64_t)nf * 128 * R > kActLdsBudget) continue;
-    const int64_t units = (int64_t)T * S;
-    const int64_t per = (units + G - 1) / G;
-    const double cost = (double)per * (nf / kWaves + 6) + 0.01 * S;
+    const int64_t per_split = G / S;                           // workgroups per k-split
+    const int64_t per = (T + per_split - 1) / per_split;       // tiles on the busiest workgroup
+    // fragments per compute wave on the busiest workgroup, plus about one fragment's time per unit for
+    // the cross-wave reduction (the weight stream keeps running through it)
+    const double cost = (double)per * (nf / kCWaves + 1.0) + 0.01 * S;
     if (cost < best_cost) { best_cost = cost; best = S; }
   }
   return best;
@@ -180,7 +184,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
   sc.part_floats[0] = sc.part_floats[1] = 0;
   auto add_gemv = [&](Phase p) -> mk_status {
     if (p.S <= 0) return fail(MK_E_CAPACITY, "no k-split of a %dx%d product fits the on-chip budget at %d rows", p.N, p.K, R);
-    if (((int64_t)p.T * p.S + G - 1) / G > kMaxUnits) return fail(MK_E_CAPACITY, "%dx%d product: too many units per workgroup", p.N, p.K);
+    if (((int64_t)p.T + G / p.S - 1) / (G / p.S) > kMaxUnits) return fail(MK_E_CAPACITY, "%dx%d product: too many units per workgroup", p.N, p.K);
     const int buf = p.out == OUT_RESID ? 1 : 0;
     if (!(p.out == OUT_LOGITS && p.S == 1)) sc.part_floats[buf] = std::max(sc.part_floats[buf], p.S * R * p.N);
     p.dst_part = buf;
@@ -195,8 +199,10 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       const int nc = (f.max_ctx + cs - 1) / cs;
       const int64_t units = (int64_t)nseq_max * f.n_kv_heads * nc;
       const double cost = (double)((units + G - 1) / G) * (cs + 48);
+      if ((int64_t)nc * (f.head_dim + 2) * 4 + (nc + 1) * 4 > kLdsBytes) continue;  // merge stages all chunks in LDS
       if (cost < best) { best = cost; sc.chunk = cs; sc.n_chunks = nc; }
     }
+    if (sc.chunk == 0) return fail(MK_E_CAPACITY, "no split-KV chunking fits max_ctx %d", f.max_ctx);
   }
   Phase e;
   memset(&e, 0, sizeof(e));
@@ -263,6 +269,12 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
     memset(&ho, 0, sizeof(ho));
     ho.type = PH_HIDDEN_OUT;
     sc.phases.push_back(ho);
+  }
+  // the weight stream of the compute waves follows the product phases in order
+  int next = -1;
+  for (int i = (int)sc.phases.size() - 1; i >= 0; --i) {
+    sc.phases[(size_t)i].next_gemv = next;
+    if (sc.phases[(size_t)i].type == PH_GEMV) next = i;
   }
   return MK_OK;
 }
@@ -473,6 +485,7 @@ void fill_args(mk_ctx *c, StepArgs &a, int R, int verify, const mk_step_io *io) 
   a.n_lin = c->n_lin;
   a.eps = f.eps;
   a.timeout_ticks = 200000000;  // 2 s at 100 MHz
+  a.trace = c->trace;
 }
 
 mk_status check_step(mk_ctx *c, const mk_step_io *io, int R, int nseq, int nrow) {
@@ -733,6 +746,18 @@ void mk_destroy(mk_ctx *c) {
   for (auto &g : c->graph)
     if (g) hipGraphExecDestroy(g);
   delete c;
+}
+
+mk_status mk_set_trace(mk_ctx *c, void *device_buffer, int64_t bytes) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  if (device_buffer) {
+    int64_t need = 0;
+    for (int r = 1; r <= kMaxRows; ++r) need = std::max<int64_t>(need, (int64_t)c->sched[r].phases.size() * c->G * 16);
+    if (bytes < need) return fail(MK_E_CAPACITY, "trace buffer %lld bytes < %lld", (long long)bytes, (long long)need);
+    if ((uintptr_t)device_buffer & 7) return fail(MK_E_ARG, "trace buffer must be 8-byte aligned");
+  }
+  c->trace = static_cast<uint64_t *>(device_buffer);
+  return MK_OK;
 }
 
 // Host-logic introspection for tests (no device needed): the phase table for a row count.

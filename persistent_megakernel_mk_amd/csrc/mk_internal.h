@@ -5,8 +5,12 @@
 
 namespace mk {
 
-constexpr int kWaves = 8;                 // compute waves per workgroup
-constexpr int kThreads = kWaves * 64;     // threads per workgroup
+constexpr int kCWaves = 4;                // weight-streaming (compute) waves per workgroup
+constexpr int kSyncWave = kCWaves;        // index of the sync wave (reductions, stores, grid barrier)
+constexpr int kWavesTotal = kCWaves + 1;
+constexpr int kThreads = kWavesTotal * 64;  // threads per workgroup
+constexpr int kCThreads = kCWaves * 64;     // threads of the compute waves
+constexpr int kRing = 12;                 // weight fragments in flight per compute wave (12 KiB)
 constexpr int kTileRows = 16;             // weight rows per MFMA tile
 constexpr int kFragK = 32;                // reduction columns per 1 KiB weight fragment
 constexpr int kLdsBytes = 160 * 1024 - 512;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU, minus static)
@@ -47,7 +51,7 @@ struct Phase {
   int64_t gain_off;  // byte offset of the bf16 RMSNorm gain (ACT_NORM)
   int32_t N, K;      // rows, columns
   int32_t T, KF;     // 16-row tiles, 32-column fragments
-  int32_t S, nf;     // k-splits, fragments per split (nf = KF / S, a multiple of kWaves)
+  int32_t S, nf;     // k-splits, fragments per split (nf = KF / S, a multiple of kCWaves)
   int32_t act, out;
   int32_t src_part, src_S, src_N, src_off;  // activation partials: buffer, splits, row stride, row offset
   int32_t dst_part;  // partial buffer written
@@ -57,7 +61,8 @@ struct Phase {
   int32_t per_channel_gate;  // 1: Kimi delta attention (gate per key channel)
   int32_t n_chunks, chunk;   // split-KV geometry
   int32_t q_off, k_off, v_off, a_off, b_off;  // row offsets inside the fused projection output
-  int32_t pad[3];
+  int32_t next_gemv;  // index of the next product phase (-1: none); the weight stream follows it
+  int32_t pad[2];
 };
 
 struct StepArgs {
@@ -102,6 +107,7 @@ struct StepArgs {
   int32_t part_stride;  // floats per partial buffer
   float eps;
   int64_t timeout_ticks;  // bound of every in-kernel wait, in s_memrealtime ticks (100 MHz)
+  uint64_t *trace;        // optional [n_phases][G][2] s_memrealtime at phase start / end of work
 };
 
 }  // namespace mk

@@ -87,6 +87,7 @@ def load() -> ctypes.CDLL:
     L.mk_read_device_status.restype = ctypes.c_int
     L.mk_destroy.argtypes, L.mk_destroy.restype = [vp], None
     L.mk_last_error.argtypes, L.mk_last_error.restype = [], ctypes.c_char_p
+    L.mk_set_trace.argtypes, L.mk_set_trace.restype = [vp, vp, ctypes.c_int64], ctypes.c_int
     L.mk_debug_phase_count.argtypes, L.mk_debug_phase_count.restype = [vp, ctypes.c_int], ctypes.c_int
     L.mk_debug_phase.argtypes, L.mk_debug_phase.restype = [vp, ctypes.c_int, ctypes.c_int, P(i32)], ctypes.c_int
     _lib = L
@@ -294,6 +295,13 @@ class Megakernel:
         check(self.lib.mk_verify_step(self.ctx, ctypes.byref(io), ctypes.c_void_p(acc.data_ptr()),
                                       ctypes.c_void_p(acc.data_ptr() + 4), _stream_ptr(stream)))
         return {"logits": logits, "argmax": argmax, "accepted_bonus": acc}
+
+    def set_trace(self, buf) -> None:
+        """buf: torch uint8/int64 device tensor (or None) receiving [phase][workgroup][2] timestamps."""
+        if buf is None:
+            check(self.lib.mk_set_trace(self.ctx, None, 0))
+        else:
+            check(self.lib.mk_set_trace(self.ctx, ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()))
 
     def device_status(self):
         s, p = i32(), i32()
