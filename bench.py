@@ -175,6 +175,27 @@ def cpu_baseline(cfg_full, layers=4):
                       f"{cfg_full.n_layers} layers ({per_token:.2f} s per token)"}
 
 
+def counter_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by
+    the calibration factors it records), or None when the kernel sources have changed since it was taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", "mk_step_kernel_c1_b1.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    info = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in ("mk_device.hip", "mk_host.cpp", "mk_internal.h"):
+        h.update(open(os.path.join(ROOT, "persistent_megakernel_mk_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != info.get("kernel_source_sha256"):
+        return None
+    return info["traffic_bytes_per_launch"]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +206,10 @@ def main() -> int:
     ap.add_argument("--no-perop", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--trace", action="store_true", help="print a per-phase breakdown of one traced step")
+    ap.add_argument("--plain-launch", action="store_true",
+                    help="ordinary (non-cooperative) launch of the same grid, for profilers")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device-to-device copy of this many MiB (a counter calibration kernel)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the megakernel runs on a single MI355X with no collectives "
@@ -199,8 +224,17 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     batches = [int(b) for b in args.batches.split(",")]
+    if args.calib_copy:
+        src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy} MiB read, {args.calib_copy} MiB written")
+        del src, dst
     cfg = synth.CONFIGS[args.config]
     m = build_gpu(cfg, max(batches))
+    if args.plain_launch:
+        m.set_launch_mode(False)
     results = {}
     for b in batches:
         r = time_steps(m, cfg, b, args.steps, args.warmup)
@@ -249,7 +283,8 @@ def main() -> int:
                                f"{cfg.ctx}-token KV cache, batch {batches[0]}",
                    "batch": batches[0], "kv_positions": cfg.ctx},
         "roofline": {"bound": "hbm", "achieved": round(h["alg_gbs"], 1), "peak": accounting.HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(h["alg_gbs"] / accounting.HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(h["alg_gbs"] / accounting.HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic() if (cfg.name == "c1" and batches[0] == 1) else None,
                      "alg_bytes_per_launch": h["alg_bytes"], "kernel": "mk_step_kernel"},
         "cpu_baseline": cpu,
         "latency_ms": {"median": round(h["median_ms"], 4), "p10": round(h["p10_ms"], 4), "p90": round(h["p90_ms"], 4)},

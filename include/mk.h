@@ -175,6 +175,13 @@ mk_status mk_read_device_status(mk_ctx *ctx, int32_t *status, int32_t *phase);
 
 void mk_destroy(mk_ctx *ctx);
 
+/* Launch mode of the persistent step kernel. cooperative != 0 (default): hipLaunchCooperativeKernel,
+ * whose runtime check guarantees that all workgroups are co-resident. cooperative == 0: an ordinary
+ * launch of the same grid (one workgroup per compute unit; each workgroup's LDS use admits only one per
+ * CU), for tools that do not follow cooperative launches; if a workgroup could not become resident,
+ * the bounded in-kernel waits expire and the step reports MK_E_DEVICE_TIMEOUT instead of hanging. */
+mk_status mk_set_launch_mode(mk_ctx *ctx, int cooperative);
+
 /* Tracing: when device_buffer is not NULL, every later step records, per phase and workgroup, two
  * 64-bit timestamps of the GPU's constant 100 MHz clock (phase start, end of the phase's work before
  * the grid barrier) at [phase][workgroup][2]. bytes must cover the longest schedule

@@ -95,6 +95,7 @@ struct mk_ctx {
   uint32_t epoch = 0;
   bool needs_reset = false;
   uint64_t *trace = nullptr;  // optional per-phase timestamps (device buffer)
+  bool cooperative = true;    // cooperative launch (co-residency guaranteed by the runtime)
   // per-op baseline graphs
   hipGraphExec_t graph[kMaxRows + 1] = {};
   const void *graph_key[kMaxRows + 1] = {};
@@ -522,9 +523,14 @@ mk_status reset_counters(mk_ctx *c, hipStream_t st) {
 }
 
 mk_status launch_step(mk_ctx *c, StepArgs &a, hipStream_t st) {
-  void *args[] = {&a};
-  HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void *>(mk_step_kernel), dim3(c->G), dim3(kThreads), args,
-                                     kLdsBytes, st));
+  if (c->cooperative) {
+    void *args[] = {&a};
+    HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void *>(mk_step_kernel), dim3(c->G), dim3(kThreads), args,
+                                       kLdsBytes, st));
+  } else {
+    hipLaunchKernelGGL(mk_step_kernel, dim3(c->G), dim3(kThreads), kLdsBytes, st, a);
+    HIP_TRY(hipGetLastError());
+  }
   return MK_OK;
 }
 
@@ -746,6 +752,12 @@ void mk_destroy(mk_ctx *c) {
   for (auto &g : c->graph)
     if (g) hipGraphExecDestroy(g);
   delete c;
+}
+
+mk_status mk_set_launch_mode(mk_ctx *c, int cooperative) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  c->cooperative = cooperative != 0;
+  return MK_OK;
 }
 
 mk_status mk_set_trace(mk_ctx *c, void *device_buffer, int64_t bytes) {

@@ -88,6 +88,7 @@ def load() -> ctypes.CDLL:
     L.mk_destroy.argtypes, L.mk_destroy.restype = [vp], None
     L.mk_last_error.argtypes, L.mk_last_error.restype = [], ctypes.c_char_p
     L.mk_set_trace.argtypes, L.mk_set_trace.restype = [vp, vp, ctypes.c_int64], ctypes.c_int
+    L.mk_set_launch_mode.argtypes, L.mk_set_launch_mode.restype = [vp, ctypes.c_int], ctypes.c_int
     L.mk_debug_phase_count.argtypes, L.mk_debug_phase_count.restype = [vp, ctypes.c_int], ctypes.c_int
     L.mk_debug_phase.argtypes, L.mk_debug_phase.restype = [vp, ctypes.c_int, ctypes.c_int, P(i32)], ctypes.c_int
     _lib = L
@@ -302,6 +303,9 @@ class Megakernel:
             check(self.lib.mk_set_trace(self.ctx, None, 0))
         else:
             check(self.lib.mk_set_trace(self.ctx, ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size()))
+
+    def set_launch_mode(self, cooperative: bool) -> None:
+        check(self.lib.mk_set_launch_mode(self.ctx, 1 if cooperative else 0))
 
     def device_status(self):
         s, p = i32(), i32()
