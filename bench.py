@@ -122,6 +122,15 @@ def trace_step(m, cfg, batch):
         a = agg.setdefault(key, [0, 0.0, 0.0, 0.0])
         a[0] += 1; a[1] += span; a[2] += work_med; a[3] += gap
     log(f"trace batch {batch}: step {total:.0f} us over {len(ph)} phases")
+    # a representative layer in detail (layer 4..7: three GDN layers and one GQA layer)
+    for i, p in enumerate(ph):
+        if p[1] in (4, 7) and p[0] != 1:
+            st = start[i] - start[i].min()
+            wk = end[i] - start[i]
+            gap = (start[i + 1].min() - end[i].max()) if i + 1 < len(ph) else 0.0
+            log(f"  L{p[1]} {PHASE_NAMES.get(p[0], p[0]):10s} N={p[2]:6d} K={p[3]:6d} S={p[6]:2d}: start skew p50 {np.median(st):5.1f} "
+                f"max {st.max():5.1f} | work p10 {np.percentile(wk, 10):6.1f} p50 {np.median(wk):6.1f} max {wk.max():6.1f} "
+                f"| span {end[i].max() - start[i].min():6.1f} | barrier {gap:5.1f} us")
     for k, (n, span, wm, gap) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
         log(f"  {k:40s} x{n:3d}: span {span:8.0f} us (median wg work {wm:8.0f}), barrier gaps {gap:7.0f} us")
     return agg
