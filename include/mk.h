@@ -108,7 +108,7 @@ typedef enum {
 /* One weight tensor in its natural layout: bf16 [rows][cols] row-major (output rows, reduction
  * columns), or NVFP4: codes uint8 [rows][cols/2] (element 2i in the low nibble), E4M3 scales uint8
  * [rows][cols/16], one fp32 tensor scale. expert: -1 for dense tensors, e >= 0 routed expert e,
- * -1 - s for shared expert s. data/scales are device pointers; they are read by kernels enqueued on
+ * -2 - s for shared expert s. data/scales are device pointers; they are read by kernels enqueued on
  * the stream passed to mk_load_weights and may be freed once that stream has synchronised. */
 typedef struct mk_weight_desc {
   int32_t layer; /* -1 for embed / final_norm / lm_head */

@@ -24,6 +24,9 @@ namespace mk {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// The step's argument block, read in place from the kernel-argument segment (constant address space)
+// wherever a member is used, rather than copied into registers.
+typedef const __attribute__((address_space(4))) StepArgs CArgs;
 
 // ---------------------------------------------------------------------------------------------
 // small helpers
@@ -57,6 +60,19 @@ __device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
   return uint4{v.x, v.y, v.z, v.w};
 }
 
+// Members of the argument block are only ever indexed with constants: a run-time index into the
+// block would make the compiler keep the whole block in vector registers.
+__device__ __forceinline__ float *part_of(CArgs &a, int i) {
+  return i == 0 ? a.part[0] : (i == 1 ? a.part[1] : a.part[2]);
+}
+__device__ __forceinline__ int pos_of(CArgs &a, int i) {
+  int p = a.pos[0];
+#pragma unroll
+  for (int k = 1; k < kMaxRows; ++k)
+    if (i == k) p = a.pos[k];
+  return p;
+}
+
 // workgroup barrier that orders LDS only (global memory is ordered explicitly where needed)
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -78,7 +94,7 @@ __device__ __forceinline__ float softplusf_(float a) { return a > 20.0f ? a : lo
 // grid barrier: two-level counters (8 groups, then one top counter), monotone across steps.
 // Run by lane 0 of the sync wave; the caller brackets it with workgroup barriers.
 // ---------------------------------------------------------------------------------------------
-__device__ bool grid_arrive_wait(const StepArgs &a, uint32_t k, int phase) {
+__device__ bool grid_arrive_wait(CArgs &a, uint32_t k, int phase) {
   const uint32_t G = gridDim.x;
   const uint32_t groups = G < 8u ? G : 8u;
   const uint32_t g = blockIdx.x % groups;
@@ -117,8 +133,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // phase descriptors are read through the constant address space, so they land in scalar registers
 // (scalar loads: they never wait behind the weight stream's vector loads)
 typedef const __attribute__((address_space(4))) Phase CPhase;
-__device__ __forceinline__ CPhase *cphase(const StepArgs &a, int q) { return (CPhase *)(a.phases + q); }
-__device__ __forceinline__ Phase load_phase(const StepArgs &a, int q) {
+__device__ __forceinline__ CPhase *cphase(CArgs &a, int q) { return (CPhase *)(a.phases + q); }
+__device__ __forceinline__ Phase load_phase(CArgs &a, int q) {
   typedef const __attribute__((address_space(4))) int32_t cint;
   Phase p;
   cint *src = (cint *)(a.phases + q);
@@ -128,40 +144,205 @@ __device__ __forceinline__ Phase load_phase(const StepArgs &a, int q) {
   return p;
 }
 
-// Work split of a product phase: the S k-splits each get gridDim.x / S workgroups (S divides the
-// workgroup count), and a split's T tiles are divided evenly over its workgroups, so every workgroup
-// works inside one k-split: tiles [t0, t1) of split s.
-__device__ __forceinline__ void unit_range(int T, int S, int &s, int &t0, int &t1) {
+// ---------------------------------------------------------------------------------------------
+// product phases: units, routing, weight stream
+// ---------------------------------------------------------------------------------------------
+
+// Per-step routing of one MoE layer, in LDS (built by every workgroup at the start of the layer's
+// first expert product and kept through the layer's second).
+struct RouteLds {
+  int32_t nseg;                     // shared experts + the routed union of the batch
+  int32_t pad[3];
+  int32_t expert[kMaxSeg];          // weight block of each segment (shared expert s -> n_exp + s)
+  float wt[kMaxSeg][kMaxRows];      // mixing weight of each segment per row (shared: 1, unrouted: 0)
+  int32_t idx[kMaxRows][kMaxTopK];  // top-k experts of each row in selection order
+  float gw[kMaxRows][kMaxTopK];     // their normalised gates
+};
+
+constexpr int kRedSlots = 8;  // unit partials in flight between the compute waves and the sync wave
+struct GemvLds {
+  static constexpr int act = 0;                                                 // kActLdsBudget bytes
+  static constexpr int red = kActLdsBudget;                                     // [kRedSlots][kCWaves][16][kMaxRows] f32
+  static constexpr int flags = red + kRedSlots * kCWaves * 16 * kMaxRows * 4;   // posted[kRedSlots], consumed[kRedSlots]
+  static constexpr int misc = flags + 2 * kRedSlots * 4;                        // rstd, finalizer flags, candidates
+  static constexpr int route = misc + 4096;                                     // RouteLds
+  static constexpr int end = route + (int)sizeof(RouteLds);
+};
+static_assert(GemvLds::end <= kLdsBytes, "product-phase LDS layout exceeds the workgroup's LDS");
+
+__device__ __forceinline__ const RouteLds *route_lds(const char *smem) {
+  return reinterpret_cast<const RouteLds *>(smem + GemvLds::route);
+}
+
+// Units of a product phase: every k-split s gets gridDim.x / S workgroups (S divides the workgroup
+// count); its units are the tiles of all segments in order (segment j, tile t -> unit j * seg_T + t),
+// divided evenly over those workgroups, so every workgroup works inside one k-split: units [u0, u1).
+__device__ __forceinline__ int phase_units(const Phase &ph, const char *smem) {
+  return ph.seg == SEG_EXPERT ? route_lds(smem)->nseg * ph.seg_T : ph.T;
+}
+__device__ __forceinline__ void unit_range(int U, int S, int &s, int &u0, int &u1) {
   const int per = (int)gridDim.x / S, wg = blockIdx.x;
   s = wg / per;
   const int wl = wg - s * per;
-  t0 = (int)(((int64_t)T * wl) / per);
-  t1 = (int)(((int64_t)T * (wl + 1)) / per);
+  u0 = (int)(((int64_t)U * wl) / per);
+  u1 = (int)(((int64_t)U * (wl + 1)) / per);
 }
 
+// Router top-k and the batch's expert union (every workgroup computes the same table from the router
+// logits z, so no extra grid barrier is needed). Per row: k passes of an argmax over z that keeps the
+// first maximum (lowest expert index on ties); gates are the sigmoids of the selected logits divided
+// by their sum, accumulated in selection order. Segments: the shared experts, then the union of the
+// rows' selections in increasing expert index. Called by all waves (three workgroup barriers).
+__device__ __forceinline__ void compute_route(CArgs &a, const Phase &ph, char *smem) {
+  RouteLds *rt = reinterpret_cast<RouteLds *>(smem + GemvLds::route);
+  const int R = a.R, E = ph.n_exp, K = ph.top_k, ns = ph.n_shared;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  float *zl = reinterpret_cast<float *>(smem + GemvLds::act);  // [R][E] router logits (staged before the product's activation)
+  const float *zp = part_of(a, ph.z_part);
+  for (int b = wave; b < R; b += kWavesTotal) {
+    float *zr = zl + b * E;
+    for (int e = lane; e < E; e += 64) {
+      float v = 0.0f;
+      for (int s2 = 0; s2 < ph.z_S; ++s2) v += ld_c(zp + ((size_t)s2 * R + b) * ph.z_N + e);
+      zr[e] = v;
+    }
+    wave_lds_sync();
+    float total = 0.0f;
+    for (int t = 0; t < K; ++t) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+      for (int e = lane; e < E; e += 64) {  // increasing e per lane: a strict > keeps the first maximum
+        const float v = zr[e];
+        if (v > bv || be == 0x7fffffff) { bv = v; be = e; }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oe = __shfl_xor(be, o);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      }
+      be = __builtin_amdgcn_readfirstlane(be);
+      bv = __shfl(bv, 0);
+      const float sg = sigmoidf_(bv);
+      total += sg;
+      if (lane == 0) {
+        zr[be] = -INFINITY;  // taken (a -inf logit is never selected over a finite one before it)
+        rt->idx[b][t] = be;
+        rt->gw[b][t] = sg;
+      }
+      wave_lds_sync();
+    }
+    if (lane < K) rt->gw[b][lane] = rt->gw[b][lane] / total;
+  }
+  lds_barrier();
+  if (wave == 0) {  // union: lane w owns experts [32 w, 32 w + 32)
+    uint32_t m = 0;
+    for (int b = 0; b < R; ++b)
+      for (int t = 0; t < K; ++t) {
+        const int e = rt->idx[b][t];
+        if ((e >> 5) == lane) m |= 1u << (e & 31);
+      }
+    const int c = __popc(m);
+    int pre = c;  // inclusive scan of the counts over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(pre, o);
+      if (lane >= o) pre += v;
+    }
+    const int total = __shfl(pre, 63);
+    int slot = ns + pre - c;
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      m &= m - 1;
+      rt->expert[slot++] = lane * 32 + bit;
+    }
+    if (lane < ns) rt->expert[lane] = E + lane;
+    if (lane == 0) rt->nseg = ns + total;
+  }
+  lds_barrier();
+  const int nseg = rt->nseg;
+  for (int i = threadIdx.x; i < nseg * R; i += kThreads) {
+    const int j = i / R, b = i % R;
+    float w = 0.0f;
+    if (j < ns) {
+      w = 1.0f;
+    } else {
+      const int e = rt->expert[j];
+      for (int t = 0; t < K; ++t)
+        if (rt->idx[b][t] == e) w = rt->gw[b][t];
+    }
+    rt->wt[j][b] = w;
+  }
+  if (blockIdx.x == 0 && a.route_idx && threadIdx.x < R * K) {
+    const int b = threadIdx.x / K, t = threadIdx.x % K;
+    a.route_idx[((size_t)ph.moe_idx * R + b) * K + t] = rt->idx[b][t];
+    if (a.route_w) a.route_w[((size_t)ph.moe_idx * R + b) * K + t] = rt->gw[b][t];
+  }
+  lds_barrier();
+}
+
+// The weight stream of one compute wave: the wave's share of every product phase, in phase order.
+// An item is one 1 KiB load per wave: a bf16 fragment (16 rows x 32 columns), or for NVFP4 the codes
+// of four fragments (16 rows x 128 columns) together with a 128-byte load of their E4M3 scales.
 struct Stream {
-  const uint4 *ptr;  // next fragment of this wave (or a valid dummy address once the stream is done)
-  int q, left, j, nfw, skip;  // skip: fragments from the end of one tile's run to the next tile's
+  const uint4 *ptr;        // next item (or a valid dummy address once the stream is done)
+  const uint32_t *sptr;    // its scales (NVFP4) or a fixed dummy word
+  int q, left, j, nfw, skip, sstep;  // phase, units left, item in run, items per run, items between runs
+  int seg, seg_left;       // current segment, units left in it
+  int route_q;             // routing this workgroup holds (phase index of its expert gate/up product)
+  int blocked;             // expert phase the stream waits at until the routing is known (-1: none)
 };
 
-__device__ __forceinline__ void stream_seek(Stream &st, const StepArgs &a, int wave, int q) {
+__device__ __forceinline__ int items_per_frag_row(const Phase &ph) { return ph.fmt == FMT_NVFP4 ? ph.KF / 4 : ph.KF; }
+
+// first item of segment seg, tile t (its own weight block for expert phases), this wave's run
+__device__ __forceinline__ void stream_at(Stream &st, CArgs &a, CPhase *ph, const char *smem, int s, int seg,
+                                          int t, int wave) {
+  const int KI = ph->fmt == FMT_NVFP4 ? ph->KF / 4 : ph->KF;
+  const int nfi = ph->fmt == FMT_NVFP4 ? ph->nf / 4 : ph->nf;
+  const uint8_t *base = a.wbuf + ph->w_off;
+  int64_t tile = t;
+  if (ph->seg == SEG_EXPERT) base += (int64_t)__builtin_amdgcn_readfirstlane(route_lds(smem)->expert[seg]) * ph->seg_stride;
+  else tile += (int64_t)seg * ph->seg_T;
+  const int64_t item = tile * KI + s * nfi + wave * st.nfw;
+  st.ptr = reinterpret_cast<const uint4 *>(base) + item * 64;
+  if (ph->fmt == FMT_NVFP4) {
+    const int Tm = ph->seg == SEG_EXPERT ? ph->seg_T : ph->T;
+    st.sptr = reinterpret_cast<const uint32_t *>(base + (int64_t)Tm * KI * 1024) + item * 32;
+  }
+}
+
+__device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *smem, int wave, int q) {
   st.q = -1;
   st.left = 0;
+  st.blocked = -1;
   st.ptr = reinterpret_cast<const uint4 *>(a.wbuf);
+  st.sptr = reinterpret_cast<const uint32_t *>(a.wbuf);
+  st.sstep = 0;
   while (q >= 0 && q < a.phase_end) {
     CPhase *ph = cphase(a, q);
     if (ph->type == PH_GEMV) {
-      int s, t0, t1;
-      unit_range(ph->T, ph->S, s, t0, t1);
-      if (t1 > t0) {
-        const int nfw = ph->nf / kCWaves;
+      if (ph->seg == SEG_EXPERT && ph->route_q != st.route_q) {  // routing not known yet: wait there
+        st.blocked = q;
+        return;
+      }
+      const int U = ph->seg == SEG_EXPERT ? __builtin_amdgcn_readfirstlane(route_lds(smem)->nseg) * ph->seg_T : ph->T;
+      int s, u0, u1;
+      unit_range(U, ph->S, s, u0, u1);
+      if (u1 > u0) {
+        const bool fp4 = ph->fmt == FMT_NVFP4;
+        const int nfi = fp4 ? ph->nf / 4 : ph->nf;
         st.q = q;
-        st.nfw = nfw;
-        st.left = (t1 - t0) * nfw;
+        st.nfw = nfi / kCWaves;
+        st.left = u1 - u0;
         st.j = 0;
-        st.skip = ph->KF - nfw;
-        st.ptr = reinterpret_cast<const uint4 *>(a.wbuf + ph->w_off) +
-                 ((int64_t)t0 * ph->KF + s * ph->nf + wave * nfw) * 64;
+        st.skip = (fp4 ? ph->KF / 4 : ph->KF) - st.nfw;
+        st.sstep = fp4 ? 32 : 0;
+        const int sT = ph->seg == SEG_EXPERT ? ph->seg_T : 0x40000000;
+        st.seg = ph->seg == SEG_EXPERT ? u0 / sT : 0;
+        const int t = ph->seg == SEG_EXPERT ? u0 - st.seg * sT : u0;
+        st.seg_left = sT - t;
+        stream_at(st, a, ph, smem, s, st.seg, t, wave);
         return;
       }
     }
@@ -169,25 +350,37 @@ __device__ __forceinline__ void stream_seek(Stream &st, const StepArgs &a, int w
   }
 }
 
-// Always issues a load (a dummy one once the stream is done), so a ring slot is only ever written by
+// Always issues both loads (dummies once the stream is done), so a ring slot is only ever written by
 // a load and its register never needs a copy that would wait for the load.
-__device__ __forceinline__ uint4 stream_take(Stream &st, const StepArgs &a, int wave, int lane) {
-  const uint4 v = ld_nt(st.ptr + lane);
+__device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *smem, int wave, int lane,
+                                            uint4 &v, uint32_t &sv) {
+  v = ld_nt(st.ptr + lane);
+  sv = __builtin_nontemporal_load(st.sptr + ((lane & 15) + 16 * (lane >> 5)));
   if (st.q >= 0) {
     st.ptr += 64;
+    st.sptr += st.sstep;
     if (++st.j == st.nfw) {
       st.j = 0;
-      st.ptr += (int64_t)st.skip * 64;
+      if (--st.left == 0) {
+        stream_seek(st, a, smem, wave, cphase(a, st.q)->next_gemv);
+      } else if (--st.seg_left == 0) {  // next expert block
+        CPhase *ph = cphase(a, st.q);
+        const int s = (int)blockIdx.x / ((int)gridDim.x / ph->S);
+        ++st.seg;
+        st.seg_left = ph->seg_T;
+        stream_at(st, a, ph, smem, s, st.seg, 0, wave);
+      } else {
+        st.ptr += (int64_t)st.skip * 64;
+        st.sptr += (int64_t)st.skip * st.sstep;
+      }
     }
-    if (--st.left == 0) stream_seek(st, a, wave, cphase(a, st.q)->next_gemv);
   }
-  return v;
 }
 
-// r[i] <- r[(i + head) % D]: puts the oldest in-flight fragment in slot 0 (waits for the ring to land)
-template <int D>
-__device__ __forceinline__ void ring_rotate(uint4 (&r)[D], int head) {
-  uint4 t[D];
+// r[i] <- r[(i + head) % D]: puts the oldest in-flight item in slot 0 (waits for the ring to land)
+template <int D, typename T>
+__device__ __forceinline__ void ring_rotate(T (&r)[D], int head) {
+  T t[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) t[i] = r[i];
 #pragma unroll
@@ -200,21 +393,13 @@ __device__ __forceinline__ void ring_rotate(uint4 (&r)[D], int head) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// GEMV phase: Y = W * act, W packed as [tile][fragment][lane][8] bf16
+// GEMV phase: Y = W * act, W packed as [tile][fragment][lane][8] bf16 (or NVFP4 groups)
 // ---------------------------------------------------------------------------------------------
-constexpr int kRedSlots = 8;  // unit partials in flight between the compute waves and the sync wave
-struct GemvLds {
-  static constexpr int act = 0;                                                 // kActLdsBudget bytes
-  static constexpr int red = kActLdsBudget;                                     // [kRedSlots][kCWaves][16][kMaxRows] f32
-  static constexpr int flags = red + kRedSlots * kCWaves * 16 * kMaxRows * 4;   // posted[kRedSlots], consumed[kRedSlots]
-  static constexpr int misc = flags + 2 * kRedSlots * 4;                        // rstd, finalizer flags, candidates
-};
-
 __device__ __forceinline__ uint32_t lds_ld(uint32_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
 
 // Bounded wait for an LDS counter written by another wave of this workgroup. On expiry the step is
 // marked timed out (status word) and the wait gives up, so every wave still reaches the kernel's end.
-__device__ __forceinline__ void lds_wait_ge(uint32_t *p, uint32_t v, const StepArgs &a) {
+__device__ __forceinline__ void lds_wait_ge(uint32_t *p, uint32_t v, CArgs &a) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   while (lds_ld(p) < v) {
     __builtin_amdgcn_s_sleep(1);
@@ -226,18 +411,31 @@ __device__ __forceinline__ void lds_wait_ge(uint32_t *p, uint32_t v, const StepA
   }
 }
 
-// Stages the activation fragments of k-split s in LDS: for each row b and column k the fp32 value y,
-// split into a bf16 high part and a bf16 low part (y - high), laid out as the B operand of
-// v_mfma_f32_16x16x32_bf16 (columns 0..R-1 high parts, R..2R-1 low parts). For an RMSNorm input, y is
-// x * gain: the per-row factor 1/rms is applied to the product's outputs (the product is linear).
-__device__ __forceinline__ void prep_act(const StepArgs &a, const Phase &ph, int s, char *smem) {
+// Activation pieces of a workgroup: one per segment its units touch when every segment has its own
+// activation; one for all (the RMSNorm input of expert gate/up products and of unsegmented products).
+__device__ __forceinline__ bool shared_act(const Phase &ph) { return ph.seg == SEG_NONE || ph.act == ACT_NORM; }
+__device__ __forceinline__ int first_piece_seg(const Phase &ph, int u0) { return shared_act(ph) ? 0 : u0 / ph.seg_T; }
+
+// Stages the activation fragments of k-split s in LDS: for each piece (segment), row b and column k
+// the fp32 value y, split into a bf16 high part and a bf16 low part (y - high), laid out as the B
+// operand of v_mfma_f32_16x16x32_bf16 (columns 0..R-1 high parts, R..2R-1 low parts). For an RMSNorm
+// input, y is x * gain: the per-row factor 1/rms is applied to the product's outputs (the product is
+// linear). Expert down products scale each row's activation by its routing weight.
+__device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u0, int u1, char *smem) {
   const int R = a.R;
   const int nk = ph.nf * kFragK;
   const int k0 = s * nk;
   uint4 *act = reinterpret_cast<uint4 *>(smem + GemvLds::act);
-  const int items = (nk / 8) * R;
+  const int j0 = first_piece_seg(ph, u0);
+  const int np = shared_act(ph) ? 1 : (u1 - 1) / ph.seg_T - j0 + 1;
+  const int per_piece = (nk / 8) * R;
+  const int items = per_piece * np;
+  const RouteLds *rt = route_lds(smem);
   for (int it = threadIdx.x; it < items; it += kThreads) {
-    const int b = it % R, kg = it / R, k = k0 + kg * 8;
+    const int pc = it / per_piece, r = it - pc * per_piece;
+    const int b = r % R, kg = r / R, k = k0 + kg * 8;
+    const int j = j0 + pc;
+    const int off = ph.src_off + j * ph.src_seg + k;
     float y[8];
     if (ph.act == ACT_NORM) {
       const float4 *xp = reinterpret_cast<const float4 *>(a.x + (size_t)b * a.H + k);
@@ -252,14 +450,14 @@ __device__ __forceinline__ void prep_act(const StepArgs &a, const Phase &ph, int
         y[e] = xs[e] * g;
       }
     } else if (ph.act == ACT_MIX) {
-      const float4 *mp = reinterpret_cast<const float4 *>(a.mix + (size_t)b * a.mix_stride + k);
+      const float4 *mp = reinterpret_cast<const float4 *>(a.mix + (size_t)b * a.mix_stride + off);
       float4 m0 = mp[0], m1 = mp[1];
       y[0] = m0.x; y[1] = m0.y; y[2] = m0.z; y[3] = m0.w; y[4] = m1.x; y[5] = m1.y; y[6] = m1.z; y[7] = m1.w;
     } else {
-      const float *src = a.part[ph.src_part];
+      const float *src = part_of(a, ph.src_part);
       float g[8] = {0, 0, 0, 0, 0, 0, 0, 0}, u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int s2 = 0; s2 < ph.src_S; ++s2) {
-        const float *row = src + ((size_t)s2 * R + b) * ph.src_N + ph.src_off + k;
+        const float *row = src + ((size_t)s2 * R + b) * ph.src_N + off;
         float4 p0 = reinterpret_cast<const float4 *>(row)[0], p1 = reinterpret_cast<const float4 *>(row)[1];
         g[0] += p0.x; g[1] += p0.y; g[2] += p0.z; g[3] += p0.w; g[4] += p1.x; g[5] += p1.y; g[6] += p1.z; g[7] += p1.w;
         if (ph.act == ACT_SWIGLU) {
@@ -268,8 +466,9 @@ __device__ __forceinline__ void prep_act(const StepArgs &a, const Phase &ph, int
           u[0] += q0.x; u[1] += q0.y; u[2] += q0.z; u[3] += q0.w; u[4] += q1.x; u[5] += q1.y; u[6] += q1.z; u[7] += q1.w;
         }
       }
+      const float w = ph.seg == SEG_EXPERT ? rt->wt[j][b] : 1.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (ph.act == ACT_SWIGLU) ? silu(g[e]) * u[e] : g[e];
+      for (int e = 0; e < 8; ++e) y[e] = (ph.act == ACT_SWIGLU) ? silu(g[e]) * u[e] * w : g[e];
     }
     uint32_t hi[4], lo[4];
 #pragma unroll
@@ -280,83 +479,130 @@ __device__ __forceinline__ void prep_act(const StepArgs &a, const Phase &ph, int
       lo[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
     const int f = kg >> 2, g4 = kg & 3;
-    act[(f * 4 + g4) * (2 * R) + b] = uint4{hi[0], hi[1], hi[2], hi[3]};
-    act[(f * 4 + g4) * (2 * R) + R + b] = uint4{lo[0], lo[1], lo[2], lo[3]};
+    uint4 *pa = act + (size_t)pc * (nk / 8) * (2 * R);
+    pa[(f * 4 + g4) * (2 * R) + b] = uint4{hi[0], hi[1], hi[2], hi[3]};
+    pa[(f * 4 + g4) * (2 * R) + R + b] = uint4{lo[0], lo[1], lo[2], lo[3]};
   }
 }
 
-// compute waves: consume this phase's fragments from the ring, refilling each slot from the stream.
+// Eight NVFP4 weights of one lane -> bf16 (exact: an E2M1 value times an E4M3 scale has at most six
+// significant bits). Element 2i is the low nibble of byte i.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ bf16x8 nvfp4_frag(uint32_t codes, float scale) {
+  f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  bf16x2 b0 = __builtin_convertvector(p0 * scale, bf16x2), b1 = __builtin_convertvector(p1 * scale, bf16x2);
+  bf16x2 b2 = __builtin_convertvector(p2 * scale, bf16x2), b3 = __builtin_convertvector(p3 * scale, bf16x2);
+  return bf16x8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
+
+// compute waves: consume this phase's items from the ring, refilling each slot from the stream.
 // A finished 16-row unit is handed to the sync wave through an LDS slot and a counter, without a
 // workgroup barrier, so the four waves never wait for each other inside a phase.
 template <int D>
-__device__ __forceinline__ void gemv_compute(const StepArgs &a, const Phase &ph, char *smem, uint4 (&ring)[D], Stream &st, int &head) {
+__device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, uint4 (&ring)[D], uint32_t (&sring)[D],
+                                         Stream &st, int &head, int s, int u0, int u1) {
   const int R = a.R;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int nfw = ph.nf / kCWaves;
-  int s, t0, t1;
-  unit_range(ph.T, ph.S, s, t0, t1);
-  const int total = (t1 - t0) * nfw;
+  const bool FP4 = ph.fmt == FMT_NVFP4;
+  const int nfw = ph.nf / kCWaves;                // fragments per unit run of this wave
+  const int ipr = FP4 ? nfw / 4 : nfw;            // ring items per unit run
+  const int total = (u1 - u0) * ipr;
   float *red = reinterpret_cast<float *>(smem + GemvLds::red);
   uint32_t *posted = reinterpret_cast<uint32_t *>(smem + GemvLds::flags);
   uint32_t *consumed = posted + kRedSlots;
+  const int piece_u4 = ph.nf * 4 * (2 * R);       // uint4 per activation piece
   const uint4 *actv = reinterpret_cast<const uint4 *>(smem + GemvLds::act);
-  if (head != 0) {
-    ring_rotate(ring, head);
-    head = 0;
-  }
-  if (total > 0) prep_act(a, ph, s, smem);
-  lds_barrier();  // activation fragments ready, handoff counters cleared
+  const bool per_seg = !shared_act(ph);
+  const int j0 = first_piece_seg(ph, u0);
   int c_j = 0, unit = 0;
+  int seg_left = per_seg ? ph.seg_T - (u0 - j0 * ph.seg_T) : 0x40000000;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int col = lane & 15, kgrp = lane >> 4;
   const uint4 *aw = actv + (size_t)wave * nfw * 4 * (2 * R);
-  // one fragment: MFMA with the activation fragment, refill the slot from the stream, close the unit
-  auto slot = [&](uint4 &r) {
-    uint4 bv = uint4{0u, 0u, 0u, 0u};
-    if (col < 2 * R) bv = aw[(c_j * 4 + kgrp) * (2 * R) + col];
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r), __builtin_bit_cast(bf16x8, bv), acc, 0,
-                                                  0, 0);
-    r = stream_take(st, a, wave, lane);  // the slot's old fragment is consumed: refill it
-    if (++c_j == nfw) {  // unit done: combine hi/lo columns and post this wave's 16 x R partials
-      float v[4];
+  auto close_unit = [&]() {  // combine hi/lo columns and post this wave's 16 x R partials
+    float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[e] + __shfl_down(acc[e], R);
-      const int sl = unit % kRedSlots;
-      const uint32_t use = (uint32_t)(unit / kRedSlots);
-      if (lds_ld(consumed + sl) < use) lds_wait_ge(consumed + sl, use, a);  // slot free (the sync wave read it)
-      float *rb = red + (sl * kCWaves + wave) * 16 * kMaxRows;
-      if (col < R) {
+    for (int e = 0; e < 4; ++e) v[e] = acc[e] + __shfl_down(acc[e], R);
+    const int sl = unit % kRedSlots;
+    const uint32_t use = (uint32_t)(unit / kRedSlots);
+    if (lds_ld(consumed + sl) < use) lds_wait_ge(consumed + sl, use, a);  // slot free (the sync wave read it)
+    float *rb = red + (sl * kCWaves + wave) * 16 * kMaxRows;
+    if (col < R) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rb[(kgrp * 4 + e) * kMaxRows + col] = v[e];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-      if (lane == 0) __hip_atomic_fetch_add(posted + sl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      ++unit;
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      c_j = 0;
+      for (int e = 0; e < 4; ++e) rb[(kgrp * 4 + e) * kMaxRows + col] = v[e];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) __hip_atomic_fetch_add(posted + sl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    ++unit;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    c_j = 0;
+    if (--seg_left == 0) {  // next segment: its own activation piece
+      aw += piece_u4;
+      seg_left = ph.seg_T;
     }
   };
-  // full turns of the ring: every slot consumed and refilled once per turn, so each fragment is waited
-  // for with D - 1 younger loads still in flight
+  // one ring item: MFMA(s) with the activation fragment(s), refill the slot from the stream
+  auto slot = [&](uint4 &r, uint32_t &sc) {
+    if (FP4) {
+      const float sc4[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sc, 0), __builtin_amdgcn_cvt_f32_fp8((int)sc, 1),
+                            __builtin_amdgcn_cvt_f32_fp8((int)sc, 2), __builtin_amdgcn_cvt_f32_fp8((int)sc, 3)};
+      const uint32_t cw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        uint4 bv = uint4{0u, 0u, 0u, 0u};
+        if (col < 2 * R) bv = aw[((c_j * 4 + f) * 4 + kgrp) * (2 * R) + col];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nvfp4_frag(cw[f], sc4[f]), __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // one fragment's dequantised weights live at a time
+      }
+    } else {
+      uint4 bv = uint4{0u, 0u, 0u, 0u};
+      if (col < 2 * R) bv = aw[(c_j * 4 + kgrp) * (2 * R) + col];
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r), __builtin_bit_cast(bf16x8, bv), acc, 0,
+                                                    0, 0);
+    }
+    stream_take(st, a, smem, wave, lane, r, sc);  // the slot's old item is consumed: refill it
+    if (++c_j == ipr) close_unit();
+  };
+  // full turns of the ring: every slot consumed and refilled once per turn, so each item is waited
+  // for with D - 1 younger items still in flight
   const int turns = total / D;
   for (int it = 0; it < turns; ++it) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) slot(ring[d]);
+    for (int d = 0; d < D; ++d) slot(ring[d], sring[d]);
   }
   const int rem = total - turns * D;
 #pragma unroll
   for (int d = 0; d < D - 1; ++d)
-    if (d < rem) slot(ring[d]);
+    if (d < rem) slot(ring[d], sring[d]);
   head = rem;
+}
+
+template <int D>
+__device__ __forceinline__ void gemv_compute(CArgs &a, const Phase &ph, char *smem, uint4 (&ring)[D], uint32_t (&sring)[D],
+                                             Stream &st, int &head) {
+  int s, u0, u1;
+  unit_range(phase_units(ph, smem), ph.S, s, u0, u1);
+  if (head != 0) {
+    ring_rotate(ring, head);
+    ring_rotate(sring, head);
+    head = 0;
+  }
+  if (u1 > u0) prep_act(a, ph, s, u0, u1, smem);
+  lds_barrier();  // activation fragments ready, handoff counters cleared
+  gemv_run(a, ph, smem, ring, sring, st, head, s, u0, u1);
 }
 
 // sync wave: activation staging (with the compute waves), norm statistics, per-unit reduction and
 // stores, finalisation
-__device__ __forceinline__ void gemv_sync(const StepArgs &a, const Phase &ph, char *smem) {
+__device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, lane = threadIdx.x & 63;
-  int s, t0, t1;
-  unit_range(ph.T, ph.S, s, t0, t1);
-  const int nunits = t1 - t0;
+  int s, u0, u1;
+  unit_range(phase_units(ph, smem), ph.S, s, u0, u1);
+  const int nunits = u1 - u0;
   float *red = reinterpret_cast<float *>(smem + GemvLds::red);
   uint32_t *posted = reinterpret_cast<uint32_t *>(smem + GemvLds::flags);
   uint32_t *consumed = posted + kRedSlots;
@@ -366,9 +612,15 @@ __device__ __forceinline__ void gemv_sync(const StepArgs &a, const Phase &ph, ch
   float *cval = misc + 16 + kMaxUnits;                       // [128]
   int *cidx = reinterpret_cast<int *>(cval + 128);           // [128]
   float *sq = cval + 256;                                    // [16][kMaxRows]
+  const RouteLds *rt = route_lds(smem);
   const bool direct = ph.out == OUT_LOGITS && ph.S == 1;
+  const bool expert = ph.seg == SEG_EXPERT;
+  // residual (and logits) finalisation: k-split partials per tile; expert down products: one partial
+  // per (segment, k-split), summed in segment-major order
+  const int S_eff = expert ? rt->nseg * ph.S : ph.S;
+  const int TN = expert ? ph.seg_T * kTileRows : ph.N;  // rows of the finalised output
   if (lane < 2 * kRedSlots) posted[lane] = 0u;  // posted[] and consumed[] (adjacent)
-  if (nunits > 0) prep_act(a, ph, s, smem);
+  if (nunits > 0) prep_act(a, ph, s, u0, u1, smem);
   lds_barrier();  // activation fragments ready, handoff counters cleared
   if (ph.act == ACT_NORM) {  // 1/rms of each row from the per-tile sums of squares (while the waves stream)
     const int nt = a.H / kTileRows;
@@ -386,9 +638,20 @@ __device__ __forceinline__ void gemv_sync(const StepArgs &a, const Phase &ph, ch
     if (ph.act == ACT_NORM && lane + 64 * k < 16 * R) rs[k] = rstd[(lane + 64 * k) % R];
   float best_v[2] = {-INFINITY, -INFINITY};
   int best_i[2] = {0x7fffffff, 0x7fffffff};
-  for (int t = t0, unit = 0; t < t1; ++t, ++unit) {
+  const float *ts = reinterpret_cast<const float *>(a.wbuf + ph.ts_off);
+  for (int u = u0, unit = 0; u < u1; ++u, ++unit) {
     const int sl = unit % kRedSlots;
     const uint32_t need = (uint32_t)(kCWaves * (unit / kRedSlots + 1));
+    int j = 0, tl = u;  // segment and tile inside it (expert phases)
+    float sc = 1.0f;
+    if (expert) {
+      j = u / ph.seg_T;
+      tl = u - j * ph.seg_T;
+      if (ph.fmt == FMT_NVFP4) {  // tensor scale of this expert's gate, up or down matrix
+        const int which = ph.out == OUT_RESID ? 2 : (tl < ph.seg_T / 2 ? 0 : 1);
+        sc = ts[rt->expert[j] * 3 + which];
+      }
+    }
     if (lds_ld(posted + sl) < need) lds_wait_ge(posted + sl, need, a);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     const float *rb = red + sl * kCWaves * 16 * kMaxRows;
@@ -400,13 +663,15 @@ __device__ __forceinline__ void gemv_sync(const StepArgs &a, const Phase &ph, ch
         float v = 0.0f;
 #pragma unroll
         for (int w = 0; w < kCWaves; ++w) v += rb[(w * 16 + row) * kMaxRows + b];
-        v *= rs[k];
-        const int n = t * kTileRows + row;
+        v *= rs[k] * sc;
         if (direct) {
+          const int n = u * kTileRows + row;
           a.logits[(size_t)b * a.V + n] = v;
           if (v > best_v[k]) { best_v[k] = v; best_i[k] = n; }
+        } else if (expert && ph.out == OUT_RESID) {
+          st_c(part_of(a, ph.dst_part) + ((size_t)(j * ph.S + s) * R + b) * TN + tl * kTileRows + row, v);
         } else {
-          st_c(a.part[ph.dst_part] + ((size_t)s * R + b) * ph.N + n, v);
+          st_c(part_of(a, ph.dst_part) + ((size_t)s * R + b) * ph.N + u * kTileRows + row, v);
         }
       }
     }
@@ -414,13 +679,17 @@ __device__ __forceinline__ void gemv_sync(const StepArgs &a, const Phase &ph, ch
     if (lane == 0) __hip_atomic_store(consumed + sl, (uint32_t)(unit / kRedSlots + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   if (ph.out == OUT_RESID || (ph.out == OUT_LOGITS && !direct)) {
-    // the last contributor of a tile adds the tile's k-split partials (in split order) into the
-    // residual (and records its sum of squares), or into the logits
+    // the last contributor of a tile adds the tile's partials (in order) into the residual (and
+    // records its sum of squares), or into the logits, and resets the tile's counter for the next step
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
     for (int i = lane; i < nunits; i += 64) {
-      const int t = t0 + i;
-      uint32_t old = __hip_atomic_fetch_add(a.fin + ph.cnt_off + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      flags[i] = (old + 1u == a.epoch * (uint32_t)ph.S) ? t : -1;
+      const int u = u0 + i;
+      const int t = expert ? u % ph.seg_T : u;
+      uint32_t *cnt = a.fin + ph.cnt_off + t;
+      const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old + 1u == (uint32_t)S_eff;
+      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      flags[i] = last ? t : -1;
     }
     wave_lds_sync();
     for (int i = 0; i < nunits; ++i) {
@@ -432,7 +701,7 @@ __device__ __forceinline__ void gemv_sync(const StepArgs &a, const Phase &ph, ch
         if (idx < 16 * R) {
           const int row = idx / R, b = idx % R, n = t * kTileRows + row;
           float v = 0.0f;
-          for (int s2 = 0; s2 < ph.S; ++s2) v += ld_c(a.part[ph.dst_part] + ((size_t)s2 * R + b) * ph.N + n);
+          for (int s2 = 0; s2 < S_eff; ++s2) v += ld_c(part_of(a, ph.dst_part) + ((size_t)s2 * R + b) * TN + n);
           if (ph.out == OUT_RESID) {
             const float xn = ld_c(a.x + (size_t)b * a.H + n) + v;
             st_c(a.x + (size_t)b * a.H + n, xn);
@@ -478,7 +747,7 @@ __device__ __forceinline__ void gemv_sync(const StepArgs &a, const Phase &ph, ch
 // ---------------------------------------------------------------------------------------------
 // gated delta rule: per (sequence, head, 16 state rows); one wave per state row, 2 channels per lane
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ void delta_phase(const StepArgs &a, const Phase &ph) {
+__device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph) {
   constexpr int kRowsPerUnit = 16;
   const int R = a.R, Hl = a.lin_heads, dk = a.dk, dv = a.dv;
   const int RB = dv / kRowsPerUnit;
@@ -487,7 +756,7 @@ __device__ __forceinline__ void delta_phase(const StepArgs &a, const Phase &ph) 
   const int G = gridDim.x, wg = blockIdx.x;
   const int u0 = (int)(((int64_t)U * wg) / G), u1 = (int)(((int64_t)U * (wg + 1)) / G);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const float *src = a.part[ph.src_part];
+  const float *src = part_of(a, ph.src_part);
   const int c0 = lane * 2;
   for (int u = u0; u < u1; ++u) {
     const int b = u / (Hl * RB), h = (u / RB) % Hl, rb = u % RB;
@@ -538,7 +807,7 @@ __device__ __forceinline__ void delta_phase(const StepArgs &a, const Phase &ph) 
 // split-KV grouped-query attention: per (sequence, kv head, chunk of positions)
 // ---------------------------------------------------------------------------------------------
 template <int HD>
-__device__ __forceinline__ void attn_phase(const StepArgs &a, const Phase &ph, char *smem) {
+__device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, nq = a.nq, nkv = a.nkv, grp = nq / nkv;
   const int CS = ph.chunk, NC = ph.n_chunks;
   const int nseq = a.verify ? 1 : R;
@@ -556,14 +825,14 @@ __device__ __forceinline__ void attn_phase(const StepArgs &a, const Phase &ph, c
   float *sc = reinterpret_cast<float *>(Vs + kAttnMaxChunk * 128);    // [Q][CS]       <= 32 KiB
   float *ml = sc + kAttnMaxQ * kAttnMaxChunk;                         // [Q][2]
   int *rpos = reinterpret_cast<int *>(ml + kAttnMaxQ * 2);            // [nrow]
-  const float *src = a.part[ph.src_part];
+  const float *src = part_of(a, ph.src_part);
   uint16_t *kc = reinterpret_cast<uint16_t *>(a.kc[ph.layer]);
   uint16_t *vc = reinterpret_cast<uint16_t *>(a.vc[ph.layer]);
 
   for (int u = u0; u < u1; ++u) {
     const int b = u / (nkv * NC), g = (u / NC) % nkv, c = u % NC;
     const int seq = a.verify ? 0 : b;
-    const int pbase = a.pos[seq];
+    const int pbase = pos_of(a, seq);
     const int maxpos = pbase + nrow - 1;
     const int c0 = c * CS;
     const int c1 = min(c0 + CS, min(a.max_ctx, maxpos + 1));  // positions [c0, c1) are read
@@ -676,7 +945,7 @@ __device__ __forceinline__ void attn_phase(const StepArgs &a, const Phase &ph, c
   }
 }
 
-__device__ __forceinline__ void merge_phase(const StepArgs &a, const Phase &ph, char *smem) {
+__device__ __forceinline__ void merge_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, nq = a.nq, hd = a.hd, NC = ph.n_chunks, W = hd + 2;
   const int U = R * nq;
   const int G = gridDim.x, wg = blockIdx.x, tid = threadIdx.x;
@@ -715,7 +984,7 @@ __device__ __forceinline__ void merge_phase(const StepArgs &a, const Phase &ph, 
   }
 }
 
-__device__ __forceinline__ void embed_phase(const StepArgs &a, const Phase &ph, char *smem) {
+__device__ __forceinline__ void embed_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, H = a.H, nt = H / kTileRows;
   const int U = R * nt;
   const int G = gridDim.x, wg = blockIdx.x, tid = threadIdx.x;
@@ -749,7 +1018,7 @@ __device__ __forceinline__ void embed_phase(const StepArgs &a, const Phase &ph, 
   }
 }
 
-__device__ __forceinline__ void final_phase(const StepArgs &a, char *smem) {
+__device__ __forceinline__ void final_phase(CArgs &a, char *smem) {
   const int R = a.R, G = gridDim.x, tid = threadIdx.x;
   float *cv = reinterpret_cast<float *>(smem);
   int *ci = reinterpret_cast<int *>(cv + G * kMaxRows);
@@ -798,7 +1067,7 @@ __device__ __forceinline__ void final_phase(const StepArgs &a, char *smem) {
   }
 }
 
-__device__ __forceinline__ void hidden_out_phase(const StepArgs &a) {
+__device__ __forceinline__ void hidden_out_phase(CArgs &a) {
   const size_t n = (size_t)a.R * a.H;
   for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
     a.hidden_out[i] = ld_c(a.x + i);
@@ -808,68 +1077,101 @@ __device__ __forceinline__ void hidden_out_phase(const StepArgs &a) {
 
 using namespace mk;
 
+// Phases that every wave runs the same way; their results are acknowledged before the grid barrier.
+__device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *smem) {
+  switch (ph.type) {
+    case PH_EMBED: embed_phase(a, ph, smem); break;
+    case PH_DELTA: delta_phase(a, ph); break;
+    case PH_ATTN:
+      if (a.hd == 64) attn_phase<64>(a, ph, smem);
+      else attn_phase<128>(a, ph, smem);
+      break;
+    case PH_MERGE: merge_phase(a, ph, smem); break;
+    case PH_FINAL: final_phase(a, smem); break;
+    case PH_HIDDEN_OUT: hidden_out_phase(a); break;
+    default: break;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+}
+
 // The step kernel: walks phases [phase_begin, phase_end) of the schedule. As a persistent launch it
 // covers the whole step with a grid barrier between phases (all workgroups co-resident: cooperative
 // launch, one workgroup per compute unit); the per-op baseline launches it once per phase.
 // Waves 0..kCWaves-1 stream weights (their ring is never drained at a phase end: the loads of the next
 // product phase are in flight through barriers and the phases in between); wave kSyncWave reduces,
-// stores cross-workgroup results and runs the grid barrier.
-extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel(StepArgs a) {
+// stores cross-workgroup results and runs the grid barrier. The two kinds of wave run separate copies
+// of the phase loop with the same sequence of workgroup barriers, so the weight ring is not live in
+// the sync wave's code.
+extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel(StepArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  (void)args;
+  CArgs *ap = (CArgs *)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ int abort_flag;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const bool is_sync = wave == kSyncWave;
-  uint32_t k = (a.epoch - 1u) * (uint32_t)a.n_barriers + (uint32_t)a.barrier_base;
-  uint4 ring[kRing];
-  Stream st;
-  int head = 0;
-  st.q = -1;
-  st.left = 0;
-  if (!is_sync) {
-    int q = a.phase_begin;
-    while (q < a.phase_end && cphase(a, q)->type != PH_GEMV) ++q;
-    stream_seek(st, a, wave, q < a.phase_end ? q : -1);
-#pragma unroll
-    for (int d = 0; d < kRing; ++d) ring[d] = stream_take(st, a, wave, lane);
-  }
-  for (int p = a.phase_begin; p < a.phase_end; ++p) {
-    const Phase ph = load_phase(a, p);
-    if (a.trace && is_sync && lane == 0) a.trace[((size_t)p * gridDim.x + blockIdx.x) * 2] = __builtin_amdgcn_s_memrealtime();
-    const bool gemv = ph.type == PH_GEMV;
-    switch (ph.type) {
-      case PH_EMBED: embed_phase(a, ph, smem); break;
-      case PH_GEMV:
-        if (is_sync) gemv_sync(a, ph, smem);
-        else gemv_compute<kRing>(a, ph, smem, ring, st, head);
-        break;
-      case PH_DELTA: delta_phase(a, ph); break;
-      case PH_ATTN:
-        if (a.hd == 64) attn_phase<64>(a, ph, smem);
-        else attn_phase<128>(a, ph, smem);
-        break;
-      case PH_MERGE: merge_phase(a, ph, smem); break;
-      case PH_FINAL: final_phase(a, smem); break;
-      case PH_HIDDEN_OUT: hidden_out_phase(a); break;
-      default: break;
-    }
-    // phase end: results stored by a wave are acknowledged before the grid barrier. In product phases
-    // only the sync wave stores; the compute waves keep their weight loads in flight.
-    if (!gemv) {
-      __builtin_amdgcn_s_waitcnt(0);
-      lds_barrier();
-    }
-    if (is_sync) {
-      __builtin_amdgcn_s_waitcnt(0);
+  int route_q = -1;  // expert gate/up phase whose routing this workgroup holds in LDS
+  if (wave == kSyncWave) {
+    uint32_t k = (ap->epoch - 1u) * (uint32_t)ap->n_barriers + (uint32_t)ap->barrier_base;
+    for (int p = ap->phase_begin; p < ap->phase_end; ++p) {
+      CArgs &a = *ap;
+      const Phase ph = load_phase(a, p);
+      if (a.trace && lane == 0) a.trace[((size_t)p * gridDim.x + blockIdx.x) * 2] = __builtin_amdgcn_s_memrealtime();
+      if (ph.type == PH_GEMV) {
+        if (ph.seg == SEG_EXPERT && route_q != ph.route_q) {
+          compute_route(a, ph, smem);
+          route_q = ph.route_q;
+        }
+        gemv_sync(a, ph, smem);
+      } else {
+        common_phase(a, ph, smem);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are acknowledged before the barrier
       if (lane == 0) {
         if (a.trace) a.trace[((size_t)p * gridDim.x + blockIdx.x) * 2 + 1] = __builtin_amdgcn_s_memrealtime();
         int ok = 1;
         if (p + 1 < a.phase_end) ok = grid_arrive_wait(a, k + 1, p);
         abort_flag = !ok;
       }
+      ++k;
+      lds_barrier();
+      if (abort_flag) return;
     }
-    ++k;
-    lds_barrier();
-    if (abort_flag) return;
+  } else {
+    uint4 ring[kRing];
+    uint32_t sring[kRing];
+    Stream st;
+    int head = 0;
+    st.route_q = -1;
+    {
+      CArgs &a = *ap;
+      int q = a.phase_begin;
+      while (q < a.phase_end && cphase(a, q)->type != PH_GEMV) ++q;
+      stream_seek(st, a, smem, wave, q < a.phase_end ? q : -1);
+#pragma unroll
+      for (int d = 0; d < kRing; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
+    }
+    for (int p = ap->phase_begin; p < ap->phase_end; ++p) {
+      CArgs &a = *ap;
+      const Phase ph = load_phase(a, p);
+      if (ph.type == PH_GEMV) {
+        if (ph.seg == SEG_EXPERT && route_q != ph.route_q) {
+          compute_route(a, ph, smem);
+          route_q = ph.route_q;
+        }
+        if (st.blocked == p) {  // the stream waited here for the routing: every ring slot is a dummy
+          st.route_q = route_q;
+          stream_seek(st, a, smem, wave, p);
+#pragma unroll
+          for (int d = 0; d < kRing; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
+          head = 0;
+        }
+        gemv_compute<kRing>(a, ph, smem, ring, sring, st, head);
+      } else {
+        common_phase(a, ph, smem);
+      }
+      lds_barrier();
+      if (abort_flag) return;
+    }
   }
 }
 
@@ -892,3 +1194,38 @@ extern "C" __global__ void mk_repack_bf16(const uint16_t *__restrict__ src, int6
     dst[((dr / 16) * KF + f) * 64 + (dr % 16) + 16 * (lane >> 4)] = v;
   }
 }
+
+// NVFP4 repacking: codes uint8 [rows][cols/2] (element 2i in the low nibble of byte i) and E4M3 scales
+// uint8 [rows][cols/16] -> the stream layout of a dst_rows x cols matrix whose rows row_off.. this
+// tensor fills (row_off a multiple of 16). Per 16-row tile t and 128-column group g, 1 KiB of codes:
+// lane l holds row l%16, columns g*128 + 32f + 8*(l/16) .. +7 in bytes 4f..4f+3 (f = 0..3, the four
+// MFMA fragments of the group). After all tiles' codes come the scales, 128 B per (t, g): word
+// r + 16h holds in byte f the scale of row r, 16-column block 8g + 2f + h (the block the lanes with
+// l/16 in {2h, 2h+1} use for fragment f).
+extern "C" __global__ void mk_repack_nvfp4(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int64_t rows,
+                                           int64_t cols, uint8_t *__restrict__ dst, int64_t row_off, int64_t dst_rows) {
+  const int64_t NG = cols / 128, T = rows / 16;
+  const int64_t total = T * NG * 64;
+  uint8_t *sdst = dst + (dst_rows / 16) * NG * 1024;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx & 63);
+    const int64_t tg = idx >> 6, t = tg / NG, g = tg - t * NG;
+    const int64_t dtg = (row_off / 16 + t) * NG + g;  // destination (tile, group)
+    const int64_t r = t * 16 + (lane & 15);
+    const int kg = lane >> 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) w[f] = *reinterpret_cast<const uint32_t *>(codes + r * (cols / 2) + g * 64 + f * 16 + kg * 4);
+    *reinterpret_cast<uint4 *>(dst + (dtg * 64 + lane) * 16) = uint4{w[0], w[1], w[2], w[3]};
+    if (lane < 32) {
+      const int64_t r2 = t * 16 + (lane & 15);
+      const int h = lane >> 4;
+      uint32_t v = 0;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) v |= (uint32_t)scales[r2 * (cols / 16) + g * 8 + 2 * f + h] << (8 * f);
+      *reinterpret_cast<uint32_t *>(sdst + (dtg * 32 + lane) * 4) = v;
+    }
+  }
+}
+
+extern "C" __global__ void mk_store_f32(float *dst, float v) { *dst = v; }

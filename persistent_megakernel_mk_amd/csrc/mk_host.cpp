@@ -24,6 +24,9 @@ using namespace mk;
 extern "C" __global__ void mk_step_kernel(StepArgs a);
 extern "C" __global__ void mk_repack_bf16(const uint16_t *src, int64_t rows, int64_t cols, uint4 *dst, int64_t row_off,
                                           int64_t KF);
+extern "C" __global__ void mk_repack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
+                                           int64_t row_off, int64_t dst_rows);
+extern "C" __global__ void mk_store_f32(float *dst, float v);
 
 namespace {
 
@@ -62,11 +65,21 @@ struct LayerSlots {
   int32_t q_off = 0, k_off = 0, v_off = 0, a_off = 0, b_off = 0;
   // required tensors (kind bitmask) and loaded tensors
   uint32_t need = 0, have = 0;
+  // mixture of experts: router, then (routed experts + shared experts) gate|up blocks and down blocks
+  Slot router;
+  int64_t ex_gu_off = -1, ex_down_off = -1, ex_gu_bytes = 0, ex_down_bytes = 0, ts_off = -1;
+  std::vector<uint8_t> ex_have;  // [(E + shared) * 3]: gate, up, down loaded
 };
+
+// Bytes of one packed matrix: bf16, or NVFP4 codes (half a byte per weight) plus one E4M3 scale per
+// 16 weights.
+int64_t matrix_bytes(int64_t rows, int64_t cols, int fmt) {
+  return fmt == FMT_NVFP4 ? rows * cols / 2 + rows * cols / 16 : rows * cols * 2;
+}
 
 struct Schedule {
   std::vector<Phase> phases;
-  int32_t part_floats[2] = {0, 0};
+  int64_t part_floats[3] = {0, 0, 0};
   int32_t n_chunks = 0, chunk = 0;
 };
 
@@ -80,12 +93,12 @@ struct mk_ctx {
   Slot embed, final_norm, lm_head;
   uint32_t global_need = 0, global_have = 0;
   int64_t packed_bytes = 0;
-  int n_lin = 0, n_resid = 0, max_rows = 1;
+  int n_lin = 0, n_resid = 0, n_moe = 0, max_rows = 1;
   std::vector<int> lin_index;  // per layer: index among linear-attention layers (-1 otherwise)
   int mix_stride = 0;
   Schedule sched[kMaxRows + 1];  // by row count
   // scratch layout (byte offsets)
-  int64_t o_status = 0, o_bar = 0, o_fin = 0, o_x = 0, o_ss = 0, o_part[2] = {0, 0}, o_mix = 0, o_attn = 0,
+  int64_t o_status = 0, o_bar = 0, o_fin = 0, o_x = 0, o_ss = 0, o_part[3] = {0, 0, 0}, o_mix = 0, o_attn = 0,
           o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxRows + 1] = {}, scratch_bytes = 0;
   int64_t kv_bytes = 0, lin_bytes = 0, latent_bytes = 0;
   // bound buffers
@@ -113,17 +126,28 @@ mk_status validate(const mk_config *c) {
   if (c->max_batch < 1 || c->max_batch > MK_MAX_BATCH) return fail(MK_E_ARG, "max_batch %d out of [1, %d]", c->max_batch, MK_MAX_BATCH);
   if (c->max_ctx < 1) return fail(MK_E_ARG, "max_ctx %d", c->max_ctx);
   if (!(c->eps > 0.0f)) return fail(MK_E_ARG, "eps must be positive");
-  bool any_gqa = false, any_lin = false;
+  bool any_gqa = false, any_lin = false, any_dense = false, any_moe = false;
   for (int l = 0; l < c->n_layers; ++l) {
     int m = c->mixer[l], f = c->ffn_kind[l];
     if (m < MK_MIXER_GQA || m > MK_MIXER_MLA) return fail(MK_E_ARG, "layer %d: bad mixer %d", l, m);
     if (f != MK_FFN_DENSE && f != MK_FFN_MOE) return fail(MK_E_ARG, "layer %d: bad ffn kind %d", l, f);
     if (m == MK_MIXER_MLA) return fail(MK_E_UNSUPPORTED, "layer %d: latent attention is not built yet", l);
-    if (f == MK_FFN_MOE) return fail(MK_E_UNSUPPORTED, "layer %d: mixture-of-experts FFN is not built yet", l);
     any_gqa |= m == MK_MIXER_GQA;
     any_lin |= m == MK_MIXER_GDN || m == MK_MIXER_KDA;
+    any_dense |= f == MK_FFN_DENSE;
+    any_moe |= f == MK_FFN_MOE;
   }
-  if (c->ffn <= 0 || c->ffn % 256) return fail(MK_E_UNSUPPORTED, "ffn %d must be a positive multiple of 256", c->ffn);
+  if (any_dense && (c->ffn <= 0 || c->ffn % 256)) return fail(MK_E_UNSUPPORTED, "ffn %d must be a positive multiple of 256", c->ffn);
+  if (any_moe) {
+    if (c->n_experts < 1 || c->n_experts > kMaxExperts) return fail(MK_E_UNSUPPORTED, "n_experts %d out of [1, %d]", c->n_experts, kMaxExperts);
+    if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_experts)
+      return fail(MK_E_UNSUPPORTED, "top_k %d out of [1, min(%d, n_experts)]", c->top_k, kMaxTopK);
+    if (c->n_shared < 0 || c->n_shared > kMaxShared) return fail(MK_E_UNSUPPORTED, "n_shared %d out of [0, %d]", c->n_shared, kMaxShared);
+    if (c->expert_format != MK_DT_BF16 && c->expert_format != MK_DT_NVFP4) return fail(MK_E_ARG, "bad expert_format %d", c->expert_format);
+    const int q = c->expert_format == MK_DT_NVFP4 ? 512 : 256;
+    if (c->expert_ffn <= 0 || c->expert_ffn % q || c->hidden % q)
+      return fail(MK_E_UNSUPPORTED, "expert_ffn %d and hidden %d must be positive multiples of %d", c->expert_ffn, c->hidden, q);
+  }
   if (any_gqa) {
     if (c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->n_q_heads % c->n_kv_heads)
       return fail(MK_E_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
@@ -142,23 +166,30 @@ mk_status validate(const mk_config *c) {
 }
 
 // Chooses the k-split count of a product: a power of two dividing the workgroup count (each
-// workgroup works inside one split), nf = KF / S a multiple of the compute-wave count, the activation
-// fragments of one split within the LDS budget, and the fewest fragment-slots on the busiest
-// workgroup (plus about one fragment's time per tile for the cross-wave reduction).
-int choose_splits(int T, int KF, int R, int G, int max_S) {
-  int best = -1;
+// workgroup works inside one split), nf = KF / S a multiple of the compute-wave count (of four times
+// it for NVFP4, whose stream items hold four fragments), the activation pieces of one workgroup within
+// the LDS budget, and the fewest fragment-slots on the busiest workgroup (plus about one fragment's
+// time per unit for the cross-wave reduction). A product of nseg segments of segT tiles each gives every
+// segment its own activation when per_seg_act (one piece per segment a workgroup's units touch).
+int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_seg_act = false, bool fp4 = false,
+                  int *pieces_out = nullptr) {
+  int best = -1, best_pieces = 1;
   double best_cost = 1e300;
-  for (int S = 1; S <= KF / kCWaves && S <= G; S *= 2) {
-    if (KF % S || (KF / S) % kCWaves || S > max_S || G % S) continue;
+  const int64_t U = (int64_t)segT * nseg;
+  const int q = fp4 ? 4 * kCWaves : kCWaves;
+  for (int S = 1; S <= KF / q && S <= G; S *= 2) {
+    if (KF % S || (KF / S) % q || S > max_S || G % S) continue;
     const int nf = KF / S;
-    if ((int64_t)nf * 128 * R > kActLdsBudget) continue;
-    const int64_t per_split = G / S;                           // workgroups per k-split
-    const int64_t per = (T + per_split - 1) / per_split;       // tiles on the busiest workgroup
-    // fragments per compute wave on the busiest workgroup, plus about one fragment's time per unit for
-    // the cross-wave reduction (the weight stream keeps running through it)
+    const int64_t per_split = G / S;                     // workgroups per k-split
+    const int64_t per = (U + per_split - 1) / per_split; // units on the busiest workgroup
+    if (per > kMaxUnits) continue;
+    const int np = per_seg_act ? (int)std::min<int64_t>((per - 1 + segT - 1) / segT + 1, nseg) : 1;
+    if (np > kMaxPieces) continue;
+    if ((int64_t)np * nf * 128 * R > kActLdsBudget) continue;
     const double cost = (double)per * (nf / kCWaves + 1.0) + 0.01 * S;
-    if (cost < best_cost) { best_cost = cost; best = S; }
+    if (cost < best_cost) { best_cost = cost; best = S; best_pieces = np; }
   }
+  if (pieces_out) *pieces_out = best_pieces;
   return best;
 }
 
@@ -171,10 +202,13 @@ Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S) {
   p.K = w.K;
   p.T = w.N / kTileRows;
   p.KF = w.K / kFragK;
-  p.S = choose_splits(p.T, p.KF, R, G, max_S);
+  p.S = choose_splits(p.T, 1, p.KF, R, G, max_S);
   p.nf = p.S > 0 ? p.KF / p.S : 0;
   p.act = act;
   p.out = out;
+  p.nseg = 1;
+  p.seg_T = p.T;
+  p.pieces = 1;
   return p;
 }
 
@@ -182,12 +216,16 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
   const mk_config &f = c->cfg;
   const int G = c->G;
   sc.phases.clear();
-  sc.part_floats[0] = sc.part_floats[1] = 0;
-  auto add_gemv = [&](Phase p) -> mk_status {
+  sc.part_floats[0] = sc.part_floats[1] = sc.part_floats[2] = 0;
+  // partial buffers: 0 = mixer inputs / router / dense gate-up, 1 = residual products, 2 = expert gate-up
+  auto add_gemv = [&](Phase p, int buf) -> mk_status {
     if (p.S <= 0) return fail(MK_E_CAPACITY, "no k-split of a %dx%d product fits the on-chip budget at %d rows", p.N, p.K, R);
-    if (((int64_t)p.T + G / p.S - 1) / (G / p.S) > kMaxUnits) return fail(MK_E_CAPACITY, "%dx%d product: too many units per workgroup", p.N, p.K);
-    const int buf = p.out == OUT_RESID ? 1 : 0;
-    if (!(p.out == OUT_LOGITS && p.S == 1)) sc.part_floats[buf] = std::max(sc.part_floats[buf], p.S * R * p.N);
+    const int64_t units = p.seg == SEG_EXPERT ? (int64_t)p.seg_T * (p.n_shared + std::min(p.n_exp, R * p.top_k)) : p.T;
+    if ((units + G / p.S - 1) / (G / p.S) > kMaxUnits) return fail(MK_E_CAPACITY, "%dx%d product: too many units per workgroup", p.N, p.K);
+    int64_t need = (int64_t)p.S * R * p.N;
+    if (p.seg == SEG_EXPERT && p.out == OUT_RESID)  // one partial per (segment, k-split)
+      need = (int64_t)(p.n_shared + std::min(p.n_exp, R * p.top_k)) * p.S * R * p.seg_T * kTileRows;
+    if (!(p.out == OUT_LOGITS && p.S == 1)) sc.part_floats[buf] = std::max(sc.part_floats[buf], need);
     p.dst_part = buf;
     sc.phases.push_back(p);
     return MK_OK;
@@ -211,13 +249,14 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
   e.w_off = c->embed.off;
   sc.phases.push_back(e);
   int resid = 0;
+  c->n_moe = 0;
   for (int l = 0; l < f.n_layers; ++l) {
     const LayerSlots &s = c->L[l];
     const int m = f.mixer[l];
     Phase p = gemv_phase(s.mix_in, ACT_NORM, OUT_PART, R, G, 64);
     p.layer = l;
     p.gain_off = s.attn_norm.off;
-    if (mk_status st = add_gemv(p)) return st;
+    if (mk_status st = add_gemv(p, 0)) return st;
     Phase mx;
     memset(&mx, 0, sizeof(mx));
     mx.layer = l;
@@ -242,25 +281,88 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
     Phase o = gemv_phase(s.wo, ACT_MIX, OUT_RESID, R, G, 68);
     o.layer = l;
     o.cnt_off = (resid++) * (f.hidden / kTileRows);
-    if (mk_status st = add_gemv(o)) return st;
-    Phase gu = gemv_phase(s.gu, ACT_NORM, OUT_PART, R, G, 64);
-    gu.layer = l;
-    gu.gain_off = s.ffn_norm.off;
-    if (mk_status st = add_gemv(gu)) return st;
-    Phase d = gemv_phase(s.wd, ACT_SWIGLU, OUT_RESID, R, G, 68);
-    d.layer = l;
-    d.src_part = 0;
-    d.src_S = gu.S;
-    d.src_N = gu.N;
-    d.cnt_off = (resid++) * (f.hidden / kTileRows);
-    if (mk_status st = add_gemv(d)) return st;
+    if (mk_status st = add_gemv(o, 1)) return st;
+    if (f.ffn_kind[l] == MK_FFN_DENSE) {
+      Phase gu = gemv_phase(s.gu, ACT_NORM, OUT_PART, R, G, 64);
+      gu.layer = l;
+      gu.gain_off = s.ffn_norm.off;
+      if (mk_status st = add_gemv(gu, 0)) return st;
+      Phase d = gemv_phase(s.wd, ACT_SWIGLU, OUT_RESID, R, G, 68);
+      d.layer = l;
+      d.src_part = 0;
+      d.src_S = gu.S;
+      d.src_N = gu.N;
+      d.cnt_off = (resid++) * (f.hidden / kTileRows);
+      if (mk_status st = add_gemv(d, 1)) return st;
+    } else {
+      // mixture of experts: router logits; gate|up of the shared experts and the batch's routed union
+      // (every workgroup derives the union from the logits); down of the same segments, each row's
+      // activation scaled by its routing weight, summed into the residual
+      const bool fp4 = f.expert_format == MK_DT_NVFP4;
+      const int F = f.expert_ffn, H = f.hidden;
+      const int nseg_max = f.n_shared + std::min(f.n_experts, R * f.top_k);
+      Phase r = gemv_phase(s.router, ACT_NORM, OUT_PART, R, G, 64);
+      r.layer = l;
+      r.gain_off = s.ffn_norm.off;
+      if (mk_status st = add_gemv(r, 0)) return st;
+      Phase gu;
+      memset(&gu, 0, sizeof(gu));
+      gu.type = PH_GEMV;
+      gu.layer = l;
+      gu.seg = SEG_EXPERT;
+      gu.fmt = fp4 ? FMT_NVFP4 : FMT_BF16;
+      gu.w_off = s.ex_gu_off;
+      gu.seg_stride = s.ex_gu_bytes;
+      gu.seg_T = 2 * F / kTileRows;
+      gu.nseg = f.n_shared;
+      gu.N = nseg_max * 2 * F;
+      gu.K = H;
+      gu.T = gu.N / kTileRows;
+      gu.KF = H / kFragK;
+      gu.S = choose_splits(gu.seg_T, nseg_max, gu.KF, R, G, 64, false, fp4, &gu.pieces);
+      gu.nf = gu.S > 0 ? gu.KF / gu.S : 0;
+      gu.act = ACT_NORM;
+      gu.gain_off = s.ffn_norm.off;
+      gu.out = OUT_PART;
+      gu.moe_idx = c->n_moe;
+      gu.n_exp = f.n_experts;
+      gu.top_k = f.top_k;
+      gu.n_shared = f.n_shared;
+      gu.z_part = 0;
+      gu.z_S = r.S;
+      gu.z_N = r.N;
+      gu.ts_off = s.ts_off;
+      gu.route_q = (int)sc.phases.size();
+      if (mk_status st = add_gemv(gu, 2)) return st;
+      Phase d = gu;
+      d.w_off = s.ex_down_off;
+      d.seg_stride = s.ex_down_bytes;
+      d.seg_T = H / kTileRows;
+      d.N = H;
+      d.K = F;
+      d.T = d.seg_T;
+      d.KF = F / kFragK;
+      d.S = choose_splits(d.seg_T, nseg_max, d.KF, R, G, 64, true, fp4, &d.pieces);
+      d.nf = d.S > 0 ? d.KF / d.S : 0;
+      d.act = ACT_SWIGLU;
+      d.gain_off = 0;
+      d.src_part = 2;
+      d.src_S = gu.S;
+      d.src_N = gu.N;
+      d.src_off = 0;
+      d.src_seg = 2 * F;
+      d.out = OUT_RESID;
+      d.cnt_off = (resid++) * (H / kTileRows);
+      if (mk_status st = add_gemv(d, 1)) return st;
+      ++c->n_moe;
+    }
   }
   c->n_resid = resid;
   if (f.vocab > 0) {
     Phase lm = gemv_phase(c->lm_head, ACT_NORM, OUT_LOGITS, R, G, 68);
     lm.gain_off = c->final_norm.off;
     lm.cnt_off = resid * (f.hidden / kTileRows);  // finalizer counters after the residual ones
-    if (mk_status st = add_gemv(lm)) return st;
+    if (mk_status st = add_gemv(lm, 0)) return st;
     Phase fin;
     memset(&fin, 0, sizeof(fin));
     fin.type = PH_FINAL;
@@ -325,13 +427,29 @@ mk_status layout(mk_ctx *c) {
                kind_bit(MK_W_O);
       c->lin_index[l] = c->n_lin++;
     }
-    s.need |= kind_bit(MK_W_ATTN_NORM) | kind_bit(MK_W_FFN_NORM) | kind_bit(MK_W_GATE) | kind_bit(MK_W_UP) |
-              kind_bit(MK_W_DOWN);
+    s.need |= kind_bit(MK_W_ATTN_NORM) | kind_bit(MK_W_FFN_NORM);
     mix_w = std::max(mix_w, inner);
     place(s.mix_in, rows, H, true);
     place(s.wo, H, inner, true);
-    place(s.gu, 2 * f.ffn, H, true);
-    place(s.wd, H, f.ffn, true);
+    if (f.ffn_kind[l] == MK_FFN_DENSE) {
+      s.need |= kind_bit(MK_W_GATE) | kind_bit(MK_W_UP) | kind_bit(MK_W_DOWN);
+      place(s.gu, 2 * f.ffn, H, true);
+      place(s.wd, H, f.ffn, true);
+    } else {
+      const int fmt = f.expert_format == MK_DT_NVFP4 ? FMT_NVFP4 : FMT_BF16;
+      const int64_t nblk = (int64_t)f.n_experts + f.n_shared;
+      s.need |= kind_bit(MK_W_ROUTER);
+      place(s.router, (int)round16(f.n_experts), H, true);
+      s.ex_gu_bytes = align_up(matrix_bytes(2LL * f.expert_ffn, H, fmt), 256);
+      s.ex_down_bytes = align_up(matrix_bytes(H, f.expert_ffn, fmt), 256);
+      s.ex_gu_off = off;
+      off += nblk * s.ex_gu_bytes;
+      s.ex_down_off = off;
+      off += nblk * s.ex_down_bytes;
+      s.ts_off = off;  // tensor scales [block][gate, up, down] (NVFP4; 1 for bf16)
+      off = align_up(off + nblk * 3 * 4, 256);
+      s.ex_have.assign((size_t)nblk * 3, 0);
+    }
   }
   if (f.vocab > 0) {
     place(c->final_norm, 1, H, false);
@@ -351,12 +469,11 @@ mk_status scratch_layout(mk_ctx *c) {
     off = align_up(off + std::max<int64_t>(bytes, 0), 256);
     return o;
   };
-  int64_t part[2] = {0, 0}, attn = 0;
+  int64_t part[3] = {0, 0, 0}, attn = 0;
   for (int r = 1; r <= kMaxRows; ++r) {
     const Schedule &s = c->sched[r];
     if (s.phases.empty()) continue;
-    part[0] = std::max<int64_t>(part[0], s.part_floats[0]);
-    part[1] = std::max<int64_t>(part[1], s.part_floats[1]);
+    for (int i = 0; i < 3; ++i) part[i] = std::max<int64_t>(part[i], s.part_floats[i]);
     if (f.n_q_heads > 0) attn = std::max<int64_t>(attn, (int64_t)r * f.n_q_heads * s.n_chunks * (f.head_dim + 2));
   }
   c->o_status = take(256);
@@ -364,8 +481,7 @@ mk_status scratch_layout(mk_ctx *c) {
   c->o_fin = take(((int64_t)c->n_resid * (H / kTileRows) + f.vocab / kTileRows) * 4);
   c->o_x = take((int64_t)R * H * 4);
   c->o_ss = take((int64_t)R * (H / kTileRows) * 4);
-  c->o_part[0] = take(part[0] * 4);
-  c->o_part[1] = take(part[1] * 4);
+  for (int i = 0; i < 3; ++i) c->o_part[i] = take(part[i] * 4);
   c->o_mix = take((int64_t)R * c->mix_stride * 4);
   c->o_attn = take(attn * 4);
   c->o_cand = take((int64_t)G * R * 2 * 4);
@@ -381,12 +497,46 @@ mk_status scratch_layout(mk_ctx *c) {
   return MK_OK;
 }
 
-// The slot and row offset that a weight descriptor fills.
+// Where a weight descriptor lands: a slot of the packed buffer (dense tensors), or an expert block.
+struct Target {
+  Slot *slot = nullptr;       // dense tensor
+  int64_t off = -1;           // expert matrix: byte offset of the packed matrix (gate|up or down)
+  int64_t mrows = 0;          // expert matrix rows (gate|up: 2F)
+  int64_t ts_off = -1;        // expert: byte offset of its tensor scale
+  uint8_t *have_flag = nullptr;
+  int fmt = FMT_BF16;
+};
+
 mk_status resolve(mk_ctx *c, const mk_weight_desc &w, Slot **slot, int64_t *row_off, int64_t *rows, int64_t *cols,
-                  uint32_t **have) {
+                  uint32_t **have, Target *tg) {
+  const mk_config &f0 = c->cfg;
+  *tg = Target();
+  if (w.expert != -1) {  // expert tensor: routed expert e >= 0, shared expert s as -2 - s
+    if (w.layer < 0 || w.layer >= f0.n_layers || f0.ffn_kind[w.layer] != MK_FFN_MOE)
+      return fail(MK_E_ARG, "expert tensor for layer %d, which has no mixture of experts", w.layer);
+    const int blk = w.expert >= 0 ? w.expert : f0.n_experts + (-2 - w.expert);
+    if ((w.expert >= 0 && w.expert >= f0.n_experts) || (w.expert < 0 && (-2 - w.expert) >= f0.n_shared))
+      return fail(MK_E_ARG, "layer %d: expert index %d out of range", w.layer, w.expert);
+    LayerSlots &s = c->L[w.layer];
+    const int F = f0.expert_ffn, H = f0.hidden;
+    tg->fmt = f0.expert_format == MK_DT_NVFP4 ? FMT_NVFP4 : FMT_BF16;
+    int which;
+    switch (w.kind) {
+      case MK_W_GATE: which = 0; *rows = F; *cols = H; *row_off = 0; break;
+      case MK_W_UP: which = 1; *rows = F; *cols = H; *row_off = F; break;
+      case MK_W_DOWN: which = 2; *rows = H; *cols = F; *row_off = 0; break;
+      default: return fail(MK_E_ARG, "layer %d: kind %d is not an expert tensor", w.layer, w.kind);
+    }
+    tg->off = which < 2 ? s.ex_gu_off + (int64_t)blk * s.ex_gu_bytes : s.ex_down_off + (int64_t)blk * s.ex_down_bytes;
+    tg->mrows = which < 2 ? 2LL * F : H;
+    tg->ts_off = s.ts_off + ((int64_t)blk * 3 + which) * 4;
+    tg->have_flag = &s.ex_have[(size_t)blk * 3 + which];
+    *slot = nullptr;
+    *have = nullptr;
+    return MK_OK;
+  }
   const mk_config &f = c->cfg;
   const int H = f.hidden;
-  if (w.expert != -1) return fail(MK_E_UNSUPPORTED, "expert tensors are not built yet");
   *row_off = 0;
   if (w.layer == -1) {
     *have = &c->global_have;
@@ -428,9 +578,19 @@ mk_status resolve(mk_ctx *c, const mk_weight_desc &w, Slot **slot, int64_t *row_
       *slot = &s.mix_in; *row_off = s.b_off; *cols = H; *rows = f.lin_heads;
       return MK_OK;
     case MK_W_O: *slot = &s.wo; *rows = H; *cols = s.wo.K; return MK_OK;
-    case MK_W_GATE: *slot = &s.gu; *rows = f.ffn; *cols = H; return MK_OK;
-    case MK_W_UP: *slot = &s.gu; *row_off = f.ffn; *rows = f.ffn; *cols = H; return MK_OK;
-    case MK_W_DOWN: *slot = &s.wd; *rows = H; *cols = f.ffn; return MK_OK;
+    case MK_W_GATE:
+      if (f.ffn_kind[w.layer] != MK_FFN_DENSE) break;
+      *slot = &s.gu; *rows = f.ffn; *cols = H; return MK_OK;
+    case MK_W_UP:
+      if (f.ffn_kind[w.layer] != MK_FFN_DENSE) break;
+      *slot = &s.gu; *row_off = f.ffn; *rows = f.ffn; *cols = H; return MK_OK;
+    case MK_W_DOWN:
+      if (f.ffn_kind[w.layer] != MK_FFN_DENSE) break;
+      *slot = &s.wd; *rows = H; *cols = f.ffn; return MK_OK;
+    case MK_W_ROUTER:
+      if (f.ffn_kind[w.layer] != MK_FFN_MOE) break;
+      *slot = &s.router; *rows = f.n_experts; *cols = H;
+      return MK_OK;
     default: break;
   }
   return fail(MK_E_ARG, "layer %d: weight kind %d does not apply to this layer", w.layer, w.kind);
@@ -454,8 +614,7 @@ void fill_args(mk_ctx *c, StepArgs &a, int R, int verify, const mk_step_io *io) 
   a.status = reinterpret_cast<int32_t *>(c->scratch + c->o_status);
   a.x = reinterpret_cast<float *>(c->scratch + c->o_x);
   a.ss = reinterpret_cast<float *>(c->scratch + c->o_ss);
-  a.part[0] = reinterpret_cast<float *>(c->scratch + c->o_part[0]);
-  a.part[1] = reinterpret_cast<float *>(c->scratch + c->o_part[1]);
+  for (int i = 0; i < 3; ++i) a.part[i] = reinterpret_cast<float *>(c->scratch + c->o_part[i]);
   a.mix = reinterpret_cast<float *>(c->scratch + c->o_mix);
   a.attn = reinterpret_cast<float *>(c->scratch + c->o_attn);
   a.cand = reinterpret_cast<float *>(c->scratch + c->o_cand);
@@ -473,6 +632,8 @@ void fill_args(mk_ctx *c, StepArgs &a, int R, int verify, const mk_step_io *io) 
   a.logits = io->logits;
   a.hidden_out = io->hidden_out;
   a.argmax = io->argmax;
+  a.route_idx = io->route_idx;
+  a.route_w = io->route_w;
   a.H = f.hidden;
   a.V = f.vocab;
   a.max_ctx = f.max_ctx;
@@ -496,8 +657,11 @@ mk_status check_step(mk_ctx *c, const mk_step_io *io, int R, int nseq, int nrow)
   if (!io) return fail(MK_E_ARG, "io is NULL");
   const mk_config &f = c->cfg;
   if (c->global_have != c->global_need) return fail(MK_E_STATE, "global weights missing (mask %x of %x)", c->global_have, c->global_need);
-  for (int l = 0; l < f.n_layers; ++l)
+  for (int l = 0; l < f.n_layers; ++l) {
     if (c->L[l].have != c->L[l].need) return fail(MK_E_STATE, "layer %d weights missing (mask %x of %x)", l, c->L[l].have, c->L[l].need);
+    for (size_t i = 0; i < c->L[l].ex_have.size(); ++i)
+      if (!c->L[l].ex_have[i]) return fail(MK_E_STATE, "layer %d: expert block %zu matrix %zu missing", l, i / 3, i % 3);
+  }
   if (!io->positions) return fail(MK_E_ARG, "positions is NULL");
   if (f.vocab > 0) {
     if (!io->tokens || !io->logits) return fail(MK_E_ARG, "tokens and logits are required");
@@ -642,7 +806,10 @@ mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
   c->epoch = 0;
   c->bound = true;
   c->global_have = 0;
-  for (auto &s : c->L) s.have = 0;
+  for (auto &s : c->L) {
+    s.have = 0;
+    std::fill(s.ex_have.begin(), s.ex_have.end(), 0);
+  }
   return MK_OK;
 }
 
@@ -656,19 +823,49 @@ mk_status mk_load_weights(mk_ctx *c, const mk_weight_desc *w, int n, void *strea
     Slot *slot;
     int64_t ro, rows, cols;
     uint32_t *have;
-    if (mk_status s = resolve(c, w[i], &slot, &ro, &rows, &cols, &have)) return s;
-    if (w[i].dtype != MK_DT_BF16) return fail(MK_E_UNSUPPORTED, "tensor %d: only bf16 dense weights are built yet", i);
+    Target tg;
+    if (mk_status s = resolve(c, w[i], &slot, &ro, &rows, &cols, &have, &tg)) return s;
+    const int want = tg.off >= 0 && tg.fmt == FMT_NVFP4 ? MK_DT_NVFP4 : MK_DT_BF16;
+    if (w[i].dtype != want)
+      return fail(MK_E_UNSUPPORTED, "tensor %d (layer %d kind %d): dtype %d, this configuration stores it as %d", i, w[i].layer,
+                  w[i].kind, w[i].dtype, want);
     if (w[i].rows != rows || w[i].cols != cols)
       return fail(MK_E_SHAPE, "tensor %d (layer %d kind %d): shape %lldx%lld, expected %lldx%lld", i, w[i].layer, w[i].kind,
                   (long long)w[i].rows, (long long)w[i].cols, (long long)rows, (long long)cols);
     if (!w[i].data || ((uintptr_t)w[i].data & 15)) return fail(MK_E_ARG, "tensor %d: data must be 16-byte aligned", i);
+    if (want == MK_DT_NVFP4) {
+      if (!w[i].scales) return fail(MK_E_ARG, "tensor %d: NVFP4 scales are required", i);
+      if (!(std::isfinite(w[i].tensor_scale))) return fail(MK_E_ARG, "tensor %d: tensor scale must be finite", i);
+    }
   }
   HIP_TRY(hipSetDevice(c->device));
   for (int i = 0; i < n; ++i) {
     Slot *slot;
     int64_t ro, rows, cols;
     uint32_t *have;
-    resolve(c, w[i], &slot, &ro, &rows, &cols, &have);
+    Target tg;
+    resolve(c, w[i], &slot, &ro, &rows, &cols, &have, &tg);
+    if (tg.off >= 0) {  // expert matrix
+      if (tg.fmt == FMT_NVFP4) {
+        const int64_t total = (rows / 16) * (cols / 128) * 64;
+        const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+        hipLaunchKernelGGL(mk_repack_nvfp4, dim3(blocks), dim3(256), 0, st, static_cast<const uint8_t *>(w[i].data),
+                           static_cast<const uint8_t *>(w[i].scales), rows, cols, c->wbuf + tg.off, ro, tg.mrows);
+        HIP_TRY(hipGetLastError());
+        hipLaunchKernelGGL(mk_store_f32, dim3(1), dim3(1), 0, st, reinterpret_cast<float *>(c->wbuf + tg.ts_off), w[i].tensor_scale);
+      } else {
+        const int64_t KF = cols / kFragK;
+        const int64_t total = ((rows + 15) / 16) * KF * 64;
+        const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+        hipLaunchKernelGGL(mk_repack_bf16, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(w[i].data), rows, cols,
+                           reinterpret_cast<uint4 *>(c->wbuf + tg.off), ro, KF);
+        HIP_TRY(hipGetLastError());
+        hipLaunchKernelGGL(mk_store_f32, dim3(1), dim3(1), 0, st, reinterpret_cast<float *>(c->wbuf + tg.ts_off), 1.0f);
+      }
+      HIP_TRY(hipGetLastError());
+      *tg.have_flag = 1;
+      continue;
+    }
     if (!slot->packed) {
       HIP_TRY(hipMemcpyAsync(c->wbuf + slot->off, w[i].data, (size_t)rows * cols * 2, hipMemcpyDeviceToDevice, st));
     } else {

@@ -19,6 +19,11 @@ constexpr int kMaxRows = 8;               // rows per step (batch or verify bloc
 constexpr int kAttnMaxChunk = 128;        // positions per split-KV chunk
 constexpr int kMaxUnits = 512;            // product units (tile x k-split) per workgroup and phase
 constexpr int kAttnMaxQ = 64;             // queries per split-KV unit (query heads per kv head x rows)
+constexpr int kMaxTopK = 16;              // routed experts per token
+constexpr int kMaxExperts = 1024;         // routed experts per MoE layer
+constexpr int kMaxShared = 4;             // shared experts per MoE layer
+constexpr int kMaxSeg = kMaxShared + kMaxRows * kMaxTopK;  // expert segments of one MoE product phase
+constexpr int kMaxPieces = 4;             // activation pieces (segment x k-split) staged per workgroup
 
 enum PhaseType : int32_t {
   PH_EMBED = 1,      // residual x <- embedding rows (or hidden_in); per-tile sums of squares
@@ -27,7 +32,17 @@ enum PhaseType : int32_t {
   PH_ATTN = 4,       // split-KV grouped-query attention partials (+ RoPE and K/V append)
   PH_MERGE = 5,      // log-sum-exp merge of the split-KV partials
   PH_FINAL = 6,      // argmax over LM-head candidates; verify accept + state commit
-  PH_HIDDEN_OUT = 7  // slice configs: x -> hidden_out
+  PH_HIDDEN_OUT = 7, // slice configs: x -> hidden_out
+  PH_MLA = 8,        // split-KV absorbed latent attention partials (+ RoPE and latent append), MFMA
+  PH_MLA_MERGE = 9   // log-sum-exp merge of the latent attention partials
+};
+
+// Segmented products: the phase's tiles belong to segments with their own activation (and, for
+// experts, their own weight block chosen at run time by the router).
+enum SegKind : int32_t {
+  SEG_NONE = 0,     // one matrix, one activation per k-split
+  SEG_HEADS = 1,    // consecutive blocks of seg_T tiles, each with its own activation slice (per head)
+  SEG_EXPERT = 2    // expert weight blocks (shared experts, then the batch's routed union), chosen per step
 };
 
 enum ActKind : int32_t {
@@ -35,6 +50,11 @@ enum ActKind : int32_t {
   ACT_PART = 1,   // y = sum over S_src partials of the previous product
   ACT_SWIGLU = 2, // y = silu(sum gate partials) * (sum up partials); up rows follow gate rows
   ACT_MIX = 3     // y = mixer output vector
+};
+
+enum WeightFmt : int32_t {
+  FMT_BF16 = 0,   // [tile][fragment][lane][8] bf16
+  FMT_NVFP4 = 1   // codes [tile][4-fragment group][lane][16 B], then scales [tile][group][32][4 B]
 };
 
 enum OutKind : int32_t {
@@ -62,7 +82,26 @@ struct Phase {
   int32_t n_chunks, chunk;   // split-KV geometry
   int32_t q_off, k_off, v_off, a_off, b_off;  // row offsets inside the fused projection output
   int32_t next_gemv;  // index of the next product phase (-1: none); the weight stream follows it
-  int32_t pad[2];
+  // ---- segmented products ----
+  int32_t seg;        // SegKind
+  int32_t nseg;       // static segments (heads; shared experts)
+  int32_t seg_T;      // tiles per segment
+  int32_t src_seg;    // activation source offset between consecutive segments (floats)
+  int64_t seg_stride; // bytes between consecutive expert blocks (SEG_EXPERT)
+  int32_t fmt;        // WeightFmt of the streamed matrix
+  int32_t pieces;     // activation pieces per workgroup the schedule guarantees (<= kMaxPieces)
+  // ---- mixture of experts ----
+  int32_t moe_idx;    // index among MoE layers (routing outputs)
+  int32_t route_q;    // SEG_EXPERT: phase index of the layer's expert gate/up product (owner of the routing)
+  int32_t n_exp, top_k, n_shared;
+  int32_t z_part, z_S, z_N;  // router logits: partial buffer, k-splits, row stride
+  int64_t ts_off;     // NVFP4: byte offset of the per-expert tensor scales [E + shared][3] (gate, up, down)
+  // ---- latent attention ----
+  int32_t rank, rope, nope, qk_stride;  // latent width, rotary width, no-rope query width, q row stride
+  int32_t dkv_off, kr_off;              // offsets of the new latent and rotary key in the projection
+  int32_t heads, hgroup;                // query heads, heads per unit
+  int32_t mla_src;                      // partial buffer of the absorbed queries
+  int32_t pad2;
 };
 
 struct StepArgs {
@@ -81,9 +120,11 @@ struct StepArgs {
   int32_t *status;     // [0] status, [1] phase, [2] abort flag
   float *x;            // residual [R][H]
   float *ss;           // [R][H/16] per-tile sums of squares of x
-  float *part[2];      // partial sums [S][R][N]
+  float *part[3];      // partial sums [S][R][N]
   float *mix;          // mixer outputs [R][M]
-  float *attn;         // split-KV partials [R][nq][n_chunks][hd + 2]
+  float *attn;         // split-KV partials [R][nq][n_chunks][hd + 2] (latent: [R][heads][n_chunks][rank + 2])
+  float *rope_mla;     // [max_ctx][rope/2][2] cos, sin for the latent attention's rotary part
+  void *const *lat;    // per layer latent caches
   float *cand;         // argmax candidates [G][R][2]
   const float *rope;   // [max_ctx][hd/2][2] cos, sin
   float *snap;         // verify snapshots [lin layers][8][heads][d_v][d_k]
@@ -98,6 +139,8 @@ struct StepArgs {
   float *logits;
   float *hidden_out;
   int32_t *argmax;
+  int32_t *route_idx;  // optional [n_moe][R][top_k]
+  float *route_w;
   int32_t *accepted;
   int32_t *bonus;
   // config scalars

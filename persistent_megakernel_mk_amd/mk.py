@@ -138,7 +138,7 @@ def weight_target(name: str):
     expert = -1
     if len(parts) == 3:
         tag = parts[1]
-        expert = int(tag[1:]) if tag[0] == "e" else -1 - int(tag[1:])
+        expert = int(tag[1:]) if tag[0] == "e" else -2 - int(tag[1:])  # shared expert s -> -2 - s
     return layer, _KIND_BY_SUFFIX[parts[-1]], expert
 
 
@@ -213,13 +213,23 @@ class Megakernel:
         for name in names:
             a = W[name]
             layer, kind, expert = weight_target(name)
-            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.device)
             d = WeightDesc()
-            d.layer, d.kind, d.expert, d.dtype = layer, kind, expert, 0
-            d.rows, d.cols = (1, a.shape[0]) if a.ndim == 1 else a.shape
-            d.data = t.data_ptr()
-            pending.append((d, t))
-            pend_bytes += t.numel() * 2
+            d.layer, d.kind, d.expert = layer, kind, expert
+            if hasattr(a, "codes"):  # NVFP4: codes, E4M3 scales, tensor scale
+                codes = torch.from_numpy(np.ascontiguousarray(a.codes)).to(self.device)
+                scales = torch.from_numpy(np.ascontiguousarray(a.scales)).to(self.device)
+                d.dtype = DTYPE["nvfp4"]
+                d.rows, d.cols = a.shape
+                d.data, d.scales, d.tensor_scale = codes.data_ptr(), scales.data_ptr(), float(a.tensor_scale)
+                pending.append((d, (codes, scales)))
+                pend_bytes += codes.numel() + scales.numel()
+            else:
+                t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.device)
+                d.dtype = DTYPE["bf16"]
+                d.rows, d.cols = (1, a.shape[0]) if a.ndim == 1 else a.shape
+                d.data = t.data_ptr()
+                pending.append((d, t))
+                pend_bytes += t.numel() * 2
             if pend_bytes >= chunk_bytes:
                 flush()
         flush()
@@ -256,8 +266,11 @@ class Megakernel:
         return out
 
     # ---- steps ----------------------------------------------------------------------------
-    def _io(self, tokens, hidden_in, positions, logits, hidden_out, argmax):
+    def _io(self, tokens, hidden_in, positions, logits, hidden_out, argmax, route=None):
         io = StepIO()
+        if route is not None:
+            io.route_idx = route[0].data_ptr()
+            io.route_w = route[1].data_ptr()
         io.tokens = tokens.data_ptr() if tokens is not None else None
         io.hidden_in = hidden_in.data_ptr() if hidden_in is not None else None
         self._pos = (i32 * MK_VERIFY_ROWS)(*[int(p) for p in positions])
@@ -276,16 +289,29 @@ class Megakernel:
                     torch.empty(rows, dtype=torch.int32, device=d))
         return None, torch.empty((rows, self.cfg.hidden), dtype=torch.float32, device=d), None
 
-    def decode(self, positions, tokens=None, hidden_in=None, out=None, stream=None, perop: bool = False):
-        """One decode step for len(positions) sequences. tokens/hidden_in are device tensors."""
+    @property
+    def n_moe(self) -> int:
+        return sum(1 for f in self.cfg.ffns if f == "moe")
+
+    def route_outputs(self, rows: int):
+        """Device buffers for the routing of every MoE layer: indices int32 and gates fp32 [n_moe][rows][top_k]."""
+        import torch
+
+        shp = (self.n_moe, rows, self.cfg.top_k)
+        return (torch.full(shp, -1, dtype=torch.int32, device=self.device),
+                torch.zeros(shp, dtype=torch.float32, device=self.device))
+
+    def decode(self, positions, tokens=None, hidden_in=None, out=None, stream=None, perop: bool = False, route=None):
+        """One decode step for len(positions) sequences. tokens/hidden_in are device tensors; route is an
+        optional (indices, gates) pair from route_outputs()."""
         B = len(positions)
         logits, hidden_out, argmax = out if out is not None else self.outputs(B)
-        io = self._io(tokens, hidden_in, positions, logits, hidden_out, argmax)
+        io = self._io(tokens, hidden_in, positions, logits, hidden_out, argmax, route)
         if perop:
             check(self.lib.mk_decode_step_perop(self.ctx, ctypes.byref(io), B, 0, _stream_ptr(stream)))
         else:
             check(self.lib.mk_decode_step(self.ctx, ctypes.byref(io), B, _stream_ptr(stream)))
-        return {"logits": logits, "hidden_out": hidden_out, "argmax": argmax}
+        return {"logits": logits, "hidden_out": hidden_out, "argmax": argmax, "route": route}
 
     def verify(self, position: int, tokens, out=None, acc=None, stream=None):
         import torch

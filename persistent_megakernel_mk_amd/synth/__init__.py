@@ -115,6 +115,9 @@ _reg(ModelConfig(name="c3s", n_layers=4, hidden=1024, vocab=0, mixers=_pattern(4
                  ffns=("moe",) * 4, lin_heads=4, d_k=128, d_v=128, mla_heads=4, kv_rank=512, rope_dim=64,
                  nope_dim=128, v_dim=128, n_experts=24, top_k=4, expert_ffn=512, n_shared=1, ctx=200, batch=8,
                  seed=2003))
+# variants that isolate one part of the path: Kimi delta attention with dense FFNs, and the NVFP4
+# mixture-of-experts slice with bf16 experts
+_reg(replace(CONFIGS["c1s"], name="c1s_kda", mixers=_pattern(4, 4, "gqa", "kda"), seed=2005))
 _reg(ModelConfig(name="c4s", n_layers=2, hidden=1024, vocab=0, mixers=("gqa",) * 2, ffns=("moe",) * 2,
                  n_q_heads=8, n_kv_heads=2, head_dim=128, n_experts=16, top_k=4, expert_ffn=512, n_shared=1,
                  expert_format="nvfp4", ctx=160, batch=4, seed=2004))
@@ -446,3 +449,5 @@ def draft_tokens_other(cfg: ModelConfig, n: int) -> np.ndarray:
     """Uniform integers in [0, vocab-1), used as 'a token other than the greedy one'."""
     tid = zlib.crc32(b"draft-other")
     return uniform_int(cfg.seed, tid, n, max(cfg.vocab - 1, 1))
+
+_reg(replace(CONFIGS["c4s"], name="c4s_bf16", expert_format="bf16", seed=2006))

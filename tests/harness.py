@@ -67,3 +67,30 @@ def compare_states(gpu_S, ref_S, new_positions=None):
             mask = np.ones(g.shape[2], bool)
             mask[list(new_positions)] = False
             assert np.array_equal(g[:, :, mask], ref[:, :, mask]), name
+
+
+def assert_routes(gpu_idx, gpu_w, route_log, moe_layers, tol_rel=REL_TOL):
+    """Routing parity per MoE layer and row: the selected experts and their order are identical wherever
+    the oracle's logit gaps around them exceed the rounding bound (8 * tol_rel * max |z|); a selection
+    inside a gap below the bound is a tie within rounding and only has to pick among the tied experts.
+    Gates (normalised sigmoids) agree to tol_rel. Returns the number of decisions checked exactly."""
+    exact = 0
+    for i, l in enumerate(moe_layers):
+        idxs, gws, z = route_log[l]
+        tol = 8 * tol_rel * float(np.max(np.abs(z)))
+        for b in range(idxs.shape[0]):
+            zs = z[b].astype(np.float64)
+            order = np.argsort(-zs, kind="stable")
+            K = idxs.shape[1]
+            for t in range(K):
+                gap_above = zs[order[t - 1]] - zs[order[t]] if t > 0 else np.inf
+                gap_below = zs[order[t]] - zs[order[t + 1]] if t + 1 < len(zs) else np.inf
+                if min(gap_above, gap_below) > tol:
+                    assert int(gpu_idx[i, b, t]) == int(idxs[b, t]), (l, b, t, gpu_idx[i, b].tolist(), idxs[b].tolist())
+                    exact += 1
+                else:
+                    assert abs(zs[int(gpu_idx[i, b, t])] - zs[order[t]]) <= tol, (l, b, t)
+            if np.array_equal(gpu_idx[i, b], idxs[b]):
+                e = float(np.max(np.abs(gpu_w[i, b] - gws[b])) / np.max(np.abs(gws[b])))
+                assert e < tol_rel, (l, b, e)
+    return exact
