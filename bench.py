@@ -109,6 +109,9 @@ def trace_step(m, cfg, batch):
     torch.cuda.synchronize()
     m.set_trace(None)
     t = buf.cpu().numpy().reshape(len(ph), G, 2).astype(np.float64) / 100.0  # microseconds
+    if os.environ.get("MK_TRACE_DUMP"):
+        np.save(os.environ["MK_TRACE_DUMP"] + f"_b{batch}.npy", t)
+        np.save(os.environ["MK_TRACE_DUMP"] + f"_b{batch}_phases.npy", np.array(ph))
     start, end = t[:, :, 0], t[:, :, 1]
     agg = {}
     total = (end[-1].max() - start[0].min())

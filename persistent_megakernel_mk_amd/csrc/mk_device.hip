@@ -165,7 +165,7 @@ struct GemvLds {
   static constexpr int red = kActLdsBudget;                                     // [kRedSlots][kCWaves][16][kMaxRows] f32
   static constexpr int flags = red + kRedSlots * kCWaves * 16 * kMaxRows * 4;   // posted[kRedSlots], consumed[kRedSlots]
   static constexpr int misc = flags + 2 * kRedSlots * 4;                        // rstd, finalizer flags, candidates
-  static constexpr int route = misc + 4096;                                     // RouteLds
+  static constexpr int route = misc + 8192;                                     // RouteLds
   static constexpr int end = route + (int)sizeof(RouteLds);
 };
 static_assert(GemvLds::end <= kLdsBytes, "product-phase LDS layout exceeds the workgroup's LDS");
@@ -187,6 +187,15 @@ __device__ __forceinline__ void unit_range(int U, int S, int &s, int &u0, int &u
   u0 = (int)(((int64_t)U * wl) / per);
   u1 = (int)(((int64_t)U * (wl + 1)) / per);
 }
+
+// Residual products finalise each tile in its last contributor. The workgroups of different k-splits
+// that share a tile range walk it starting at different tiles (split s starts s/S of the way in and
+// wraps), so the last contribution to the range's tiles, and with it the finalisation work, is spread
+// over those workgroups instead of falling on whichever finishes last.
+__device__ __forceinline__ bool rotated(const Phase &ph) {
+  return ph.seg == SEG_NONE && ph.S > 1 && (ph.out == OUT_RESID || ph.out == OUT_LOGITS);
+}
+__device__ __forceinline__ int rot_start(int s, int S, int n) { return (int)(((int64_t)s * n) / S); }
 
 // Router top-k and the batch's expert union (every workgroup computes the same table from the router
 // logits z, so no extra grid barrier is needed). Per row: k passes of an argmax over z that keeps the
@@ -340,9 +349,16 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
         st.sstep = fp4 ? 32 : 0;
         const int sT = ph->seg == SEG_EXPERT ? ph->seg_T : 0x40000000;
         st.seg = ph->seg == SEG_EXPERT ? u0 / sT : 0;
-        const int t = ph->seg == SEG_EXPERT ? u0 - st.seg * sT : u0;
+        int t = ph->seg == SEG_EXPERT ? u0 - st.seg * sT : u0;
         st.seg_left = sT - t;
-        stream_at(st, a, ph, smem, s, st.seg, t, wave);
+        const bool rot = ph->seg == SEG_NONE && ph->S > 1 && (ph->out == OUT_RESID || ph->out == OUT_LOGITS);
+        if (rot) {  // start r0 units in; after the range's end wrap to its first tile
+          const int r0 = rot_start(s, ph->S, u1 - u0);
+          t = u0 + r0;
+          st.seg_left = (u1 - u0) - r0;
+          st.seg = -1;  // marks the pending wrap
+        }
+        stream_at(st, a, ph, smem, s, st.seg < 0 ? 0 : st.seg, t, wave);
         return;
       }
     }
@@ -355,7 +371,7 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
 __device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *smem, int wave, int lane,
                                             uint4 &v, uint32_t &sv) {
   v = ld_nt(st.ptr + lane);
-  sv = __builtin_nontemporal_load(st.sptr + ((lane & 15) + 16 * (lane >> 5)));
+  if (st.sstep) sv = __builtin_nontemporal_load(st.sptr + ((lane & 15) + 16 * (lane >> 5)));
   if (st.q >= 0) {
     st.ptr += 64;
     st.sptr += st.sstep;
@@ -363,12 +379,20 @@ __device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *sm
       st.j = 0;
       if (--st.left == 0) {
         stream_seek(st, a, smem, wave, cphase(a, st.q)->next_gemv);
-      } else if (--st.seg_left == 0) {  // next expert block
+      } else if (--st.seg_left == 0) {  // next expert block, or the wrap of a rotated range
         CPhase *ph = cphase(a, st.q);
-        const int s = (int)blockIdx.x / ((int)gridDim.x / ph->S);
-        ++st.seg;
-        st.seg_left = ph->seg_T;
-        stream_at(st, a, ph, smem, s, st.seg, 0, wave);
+        const int per = (int)gridDim.x / ph->S;
+        const int s = (int)blockIdx.x / per;
+        if (st.seg < 0) {
+          const int wl = (int)blockIdx.x - s * per;
+          st.seg = 0;
+          st.seg_left = 0x40000000;
+          stream_at(st, a, ph, smem, s, 0, (int)(((int64_t)ph->T * wl) / per), wave);
+        } else {
+          ++st.seg;
+          st.seg_left = ph->seg_T;
+          stream_at(st, a, ph, smem, s, st.seg, 0, wave);
+        }
       } else {
         st.ptr += (int64_t)st.skip * 64;
         st.sptr += (int64_t)st.skip * st.sstep;
@@ -428,12 +452,15 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
   uint4 *act = reinterpret_cast<uint4 *>(smem + GemvLds::act);
   const int j0 = first_piece_seg(ph, u0);
   const int np = shared_act(ph) ? 1 : (u1 - 1) / ph.seg_T - j0 + 1;
-  const int per_piece = (nk / 8) * R;
-  const int items = per_piece * np;
   const RouteLds *rt = route_lds(smem);
-  for (int it = threadIdx.x; it < items; it += kThreads) {
-    const int pc = it / per_piece, r = it - pc * per_piece;
-    const int b = r % R, kg = r / R, k = k0 + kg * 8;
+  // each thread keeps one row b and walks the 8-column groups with a fixed stride (no divisions)
+  const int tpr = kThreads / R;  // threads per row
+  const int b = (int)threadIdx.x % R, kg0 = (int)threadIdx.x / R;
+  const int ngroups = (nk / 8) * np;
+  for (int gi = kg0; threadIdx.x < tpr * R && gi < ngroups; gi += tpr) {
+    int pc = 0, kg = gi;
+    while (kg >= nk / 8) { kg -= nk / 8; ++pc; }
+    const int k = k0 + kg * 8;
     const int j = j0 + pc;
     const int off = ph.src_off + j * ph.src_seg + k;
     float y[8];
@@ -485,6 +512,115 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
   }
 }
 
+// Product phases whose tiles are completed by their last contributor (residual adds, split logits).
+__device__ __forceinline__ bool needs_finalise(const Phase &ph) {
+  return ph.out == OUT_RESID || (ph.out == OUT_LOGITS && ph.S > 1);
+}
+
+// Finalisation of one tile by the sync wave: every lane sums (row, b) values of the tile over the
+// partials in partial order (plus the residual), four partials' loads in flight at a time;
+// device-coherent loads read the other contributors' partials (no cache invalidation). Stores the
+// residual and the tile's sums of squares, or the logits and the argmax candidate of each row (kept by
+// lane b).
+__device__ __forceinline__ void finalise_tiles(CArgs &a, const Phase &ph, int tile, int S_eff, int TN, float &best_v,
+                                               int &best_i) {
+  const int nfin = 1;
+  const int R = a.R, lane = threadIdx.x & 63;
+  const float *pp = part_of(a, ph.dst_part);
+  const size_t pstride = (size_t)R * TN;
+  const bool resid = ph.out == OUT_RESID;
+  int row_k[2], b_k[2];
+  bool ok_k[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = lane + 64 * k;
+    ok_k[k] = idx < 16 * R;
+    b_k[k] = ok_k[k] ? idx >> 4 : 0;  // lanes 16 b .. 16 b + 15: the tile's 16 rows of row b
+    row_k[k] = idx & 15;
+  }
+  float kb_v[2] = {-INFINITY, -INFINITY};  // logits: best of this lane's (row b_k) values
+  int kb_i[2] = {0x7fffffff, 0x7fffffff};
+  for (int f0 = 0; f0 < nfin; f0 += 4) {
+    int tq[4];
+    float acc[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tq[q] = f0 + q < nfin ? tile : -1;
+      acc[q][0] = acc[q][1] = 0.0f;
+    }
+    size_t off[4][2];  // element offsets (a valid dummy for lanes or tiles without a value)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        off[q][k] = (tq[q] >= 0 && ok_k[k]) ? (size_t)b_k[k] * TN + tq[q] * kTileRows + row_k[k] : 0;
+    // four partials of the eight values per round: 32 loads issued before the first add (in order)
+    for (int s0 = 0; s0 < S_eff; s0 += 4) {
+      float t[4][4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float *ps = pp + (size_t)min(s0 + j, S_eff - 1) * pstride;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) t[j][q][k] = ld_c(ps + off[q][k]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (s0 + j < S_eff) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) acc[q][k] += t[j][q][k];
+        }
+    }
+    float xv[4][2];  // the residual values these tiles update (loaded together)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        xv[q][k] = resid ? ld_c(a.x + ((tq[q] >= 0 && ok_k[k]) ? (size_t)b_k[k] * a.H + tq[q] * kTileRows + row_k[k] : 0)) : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (tq[q] < 0) continue;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int n = tq[q] * kTileRows + row_k[k], b = b_k[k];
+        float v = acc[q][k];
+        if (resid) {
+          if (ok_k[k]) {
+            v += xv[q][k];
+            st_c(a.x + (size_t)b * a.H + n, v);
+          }
+          float q2 = ok_k[k] ? v * v : 0.0f;  // sum of squares over the tile's 16 rows (16 consecutive lanes)
+#pragma unroll
+          for (int o = 8; o >= 1; o >>= 1) q2 += __shfl_xor(q2, o);
+          if (ok_k[k] && row_k[k] == 0) st_c(a.ss + (size_t)b * (a.H / kTileRows) + tq[q], q2);
+        } else if (ok_k[k]) {
+          a.logits[(size_t)b * a.V + n] = v;
+          if (v > kb_v[k] || (v == kb_v[k] && n < kb_i[k])) { kb_v[k] = v; kb_i[k] = n; }
+        }
+      }
+    }
+  }
+  if (!resid) {  // per row: the first maximum over the finalised tiles, kept by lane b
+    for (int b = 0; b < R; ++b) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (ok_k[k] && b_k[k] == b) { bv = kb_v[k]; bi = kb_i[k]; }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (lane == b && (bv > best_v || (bv == best_v && bi < best_i))) { best_v = bv; best_i = bi; }
+    }
+  }
+}
+
 // Eight NVFP4 weights of one lane -> bf16 (exact: an E2M1 value times an E4M3 scale has at most six
 // significant bits). Element 2i is the low nibble of byte i.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -502,12 +638,12 @@ __device__ __forceinline__ bf16x8 nvfp4_frag(uint32_t codes, float scale) {
 // compute waves: consume this phase's items from the ring, refilling each slot from the stream.
 // A finished 16-row unit is handed to the sync wave through an LDS slot and a counter, without a
 // workgroup barrier, so the four waves never wait for each other inside a phase.
-template <int D>
+template <bool HAS_FP4, int D>
 __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, uint4 (&ring)[D], uint32_t (&sring)[D],
                                          Stream &st, int &head, int s, int u0, int u1) {
   const int R = a.R;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const bool FP4 = ph.fmt == FMT_NVFP4;
+  const bool FP4 = HAS_FP4 && ph.fmt == FMT_NVFP4;
   const int nfw = ph.nf / kCWaves;                // fragments per unit run of this wave
   const int ipr = FP4 ? nfw / 4 : nfw;            // ring items per unit run
   const int total = (u1 - u0) * ipr;
@@ -581,7 +717,7 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
   head = rem;
 }
 
-template <int D>
+template <bool HAS_FP4, int D>
 __device__ __forceinline__ void gemv_compute(CArgs &a, const Phase &ph, char *smem, uint4 (&ring)[D], uint32_t (&sring)[D],
                                              Stream &st, int &head) {
   int s, u0, u1;
@@ -593,7 +729,7 @@ __device__ __forceinline__ void gemv_compute(CArgs &a, const Phase &ph, char *sm
   }
   if (u1 > u0) prep_act(a, ph, s, u0, u1, smem);
   lds_barrier();  // activation fragments ready, handoff counters cleared
-  gemv_run(a, ph, smem, ring, sring, st, head, s, u0, u1);
+  gemv_run<HAS_FP4>(a, ph, smem, ring, sring, st, head, s, u0, u1);
 }
 
 // sync wave: activation staging (with the compute waves), norm statistics, per-unit reduction and
@@ -611,7 +747,6 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   int *flags = reinterpret_cast<int *>(misc + 16);           // [kMaxUnits]
   float *cval = misc + 16 + kMaxUnits;                       // [128]
   int *cidx = reinterpret_cast<int *>(cval + 128);           // [128]
-  float *sq = cval + 256;                                    // [16][kMaxRows]
   const RouteLds *rt = route_lds(smem);
   const bool direct = ph.out == OUT_LOGITS && ph.S == 1;
   const bool expert = ph.seg == SEG_EXPERT;
@@ -639,7 +774,10 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   float best_v[2] = {-INFINITY, -INFINITY};
   int best_i[2] = {0x7fffffff, 0x7fffffff};
   const float *ts = reinterpret_cast<const float *>(a.wbuf + ph.ts_off);
-  for (int u = u0, unit = 0; u < u1; ++u, ++unit) {
+  const int nrot = u1 - u0, r0 = rotated(ph) ? rot_start(s, ph.S, nrot) : 0;
+  const bool fin = needs_finalise(ph);
+  for (int unit = 0; unit < nrot; ++unit) {
+    const int u = u0 + (r0 + unit < nrot ? r0 + unit : r0 + unit - nrot);
     const int sl = unit % kRedSlots;
     const uint32_t need = (uint32_t)(kCWaves * (unit / kRedSlots + 1));
     int j = 0, tl = u;  // segment and tile inside it (expert phases)
@@ -677,50 +815,19 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_store(consumed + sl, (uint32_t)(unit / kRedSlots + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  if (ph.out == OUT_RESID || (ph.out == OUT_LOGITS && !direct)) {
-    // the last contributor of a tile adds the tile's partials (in order) into the residual (and
-    // records its sum of squares), or into the logits, and resets the tile's counter for the next step
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are acknowledged
-    for (int i = lane; i < nunits; i += 64) {
-      const int u = u0 + i;
-      const int t = expert ? u % ph.seg_T : u;
-      uint32_t *cnt = a.fin + ph.cnt_off + t;
-      const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = old + 1u == (uint32_t)S_eff;
-      if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      flags[i] = last ? t : -1;
-    }
-    wave_lds_sync();
-    for (int i = 0; i < nunits; ++i) {
-      const int t = flags[i];
-      if (t < 0) continue;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int idx = lane + 64 * k;
-        if (idx < 16 * R) {
-          const int row = idx / R, b = idx % R, n = t * kTileRows + row;
-          float v = 0.0f;
-          for (int s2 = 0; s2 < S_eff; ++s2) v += ld_c(part_of(a, ph.dst_part) + ((size_t)s2 * R + b) * TN + n);
-          if (ph.out == OUT_RESID) {
-            const float xn = ld_c(a.x + (size_t)b * a.H + n) + v;
-            st_c(a.x + (size_t)b * a.H + n, xn);
-            sq[row * kMaxRows + b] = xn * xn;
-          } else {
-            a.logits[(size_t)b * a.V + n] = v;
-            if (v > best_v[k] || (v == best_v[k] && n < best_i[k])) { best_v[k] = v; best_i[k] = n; }
-          }
-        }
+    if (fin) {
+      // count this contribution as soon as its partials are acknowledged; the last contributor of the
+      // tile finalises it right away (while the compute waves stream the remaining units) and resets
+      // the tile's counter for the next step
+      __builtin_amdgcn_s_waitcnt(0);
+      int last = 0;
+      if (lane == 0) {
+        uint32_t *cnt = a.fin + ph.cnt_off + tl;
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old + 1u == (uint32_t)S_eff;
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (ph.out == OUT_RESID) {
-        wave_lds_sync();
-        if (lane < R) {
-          float v = 0.0f;
-          for (int row = 0; row < 16; ++row) v += sq[row * kMaxRows + lane];
-          st_c(a.ss + (size_t)lane * (a.H / kTileRows) + t, v);
-        }
-        wave_lds_sync();
-      }
+      if (__shfl(last, 0)) finalise_tiles(a, ph, tl, S_eff, TN, best_v[0], best_i[0]);
     }
   }
   if (ph.out == OUT_LOGITS) {  // per-workgroup argmax candidate of each row (first index on ties)
@@ -1103,9 +1210,8 @@ __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *sm
 // stores cross-workgroup results and runs the grid barrier. The two kinds of wave run separate copies
 // of the phase loop with the same sequence of workgroup barriers, so the weight ring is not live in
 // the sync wave's code.
-extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel(StepArgs args) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  (void)args;
+template <bool HAS_FP4>
+__device__ __forceinline__ void step_body(char *smem) {
   CArgs *ap = (CArgs *)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ int abort_flag;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1165,7 +1271,7 @@ extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel(StepArgs a
           for (int d = 0; d < kRing; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
           head = 0;
         }
-        gemv_compute<kRing>(a, ph, smem, ring, sring, st, head);
+        gemv_compute<HAS_FP4, kRing>(a, ph, smem, ring, sring, st, head);
       } else {
         common_phase(a, ph, smem);
       }
@@ -1173,6 +1279,20 @@ extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel(StepArgs a
       if (abort_flag) return;
     }
   }
+}
+
+// Two builds of the same step: without NVFP4 products (the bf16 weight stream alone in the product
+// loop) and with them (each ring item is either a bf16 fragment or four NVFP4 fragments).
+extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel(StepArgs args) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  (void)args;
+  step_body<false>(smem);
+}
+
+extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel_nvfp4(StepArgs args) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  (void)args;
+  step_body<true>(smem);
 }
 
 // Weight repacking: natural bf16 [rows][cols] -> tile-major MFMA fragments. Fragment (t, f) holds, for

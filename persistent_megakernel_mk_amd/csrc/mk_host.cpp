@@ -22,6 +22,7 @@
 using namespace mk;
 
 extern "C" __global__ void mk_step_kernel(StepArgs a);
+extern "C" __global__ void mk_step_kernel_nvfp4(StepArgs a);
 extern "C" __global__ void mk_repack_bf16(const uint16_t *src, int64_t rows, int64_t cols, uint4 *dst, int64_t row_off,
                                           int64_t KF);
 extern "C" __global__ void mk_repack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
@@ -109,6 +110,7 @@ struct mk_ctx {
   bool needs_reset = false;
   uint64_t *trace = nullptr;  // optional per-phase timestamps (device buffer)
   bool cooperative = true;    // cooperative launch (co-residency guaranteed by the runtime)
+  bool nvfp4 = false;         // the schedule has NVFP4 products: the step kernel build that decodes them
   // per-op baseline graphs
   hipGraphExec_t graph[kMaxRows + 1] = {};
   const void *graph_key[kMaxRows + 1] = {};
@@ -686,14 +688,16 @@ mk_status reset_counters(mk_ctx *c, hipStream_t st) {
   return MK_OK;
 }
 
+const void *step_kernel(const mk_ctx *c) {
+  return c->nvfp4 ? reinterpret_cast<const void *>(mk_step_kernel_nvfp4) : reinterpret_cast<const void *>(mk_step_kernel);
+}
+
 mk_status launch_step(mk_ctx *c, StepArgs &a, hipStream_t st) {
+  void *args[] = {&a};
   if (c->cooperative) {
-    void *args[] = {&a};
-    HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void *>(mk_step_kernel), dim3(c->G), dim3(kThreads), args,
-                                       kLdsBytes, st));
+    HIP_TRY(hipLaunchCooperativeKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
   } else {
-    hipLaunchKernelGGL(mk_step_kernel, dim3(c->G), dim3(kThreads), kLdsBytes, st, a);
-    HIP_TRY(hipGetLastError());
+    HIP_TRY(hipLaunchKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
   }
   return MK_OK;
 }
@@ -712,6 +716,8 @@ mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
   c->cfg = *cfg;
   c->device = hip_device;
   c->max_rows = cfg->vocab > 0 ? kMaxRows : cfg->max_batch;
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (cfg->ffn_kind[l] == MK_FFN_MOE && cfg->expert_format == MK_DT_NVFP4) c->nvfp4 = true;
   if (hip_device >= 0) {
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, hip_device);
@@ -735,10 +741,10 @@ mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
   if (hip_device >= 0) {
     hipError_t e = hipSetDevice(hip_device);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void *>(mk_step_kernel), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      e = hipFuncSetAttribute(step_kernel(c), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) { delete c; return fail(MK_E_HIP, "kernel setup: %s", hipGetErrorString(e)); }
     int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void *>(mk_step_kernel), kThreads, kLdsBytes);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, step_kernel(c), kThreads, kLdsBytes);
     if (e != hipSuccess || nb < 1) {
       delete c;
       return fail(MK_E_HIP, "step kernel cannot be resident (%d per CU): %s", nb, hipGetErrorString(e));
@@ -926,8 +932,8 @@ mk_status mk_decode_step_perop(mk_ctx *c, const mk_step_io *io, int batch, int u
     a.phase_begin = p;
     a.phase_end = p + 1;
     a.barrier_base = p;
-    hipLaunchKernelGGL(mk_step_kernel, dim3(c->G), dim3(kThreads), kLdsBytes, st, a);
-    HIP_TRY(hipGetLastError());
+    void *args[] = {&a};
+    HIP_TRY(hipLaunchKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
   }
   return MK_OK;
 }
