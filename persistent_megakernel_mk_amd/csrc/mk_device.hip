@@ -1052,8 +1052,255 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// absorbed multi-head latent attention: split-KV partials per (query row, chunk, head group)
+// ---------------------------------------------------------------------------------------------
+// The page "Kimi K3's TPU megakernel ..." (section "How it maps onto a TPU v7") runs latent attention
+// in its absorbed form over a cache of latents: with q~_h = W_uk,h^T q_nope,h, every head scores
+// s_j = (q~_h . c_j + q_rope,h . k_rope,j) / sqrt(nope + rope) against the shared [c_j | k_rope,j] row
+// and reads out sum_j p_j c_j (the value up-projection follows as a separate product). Both
+// contractions are dense: per 64-position block, scores = C (64 x D) * Q^T (D x heads) and
+// out^T += C^T (rank x 64) * P (64 x heads) run on v_mfma_f32_16x16x32_bf16 with the latent rows as
+// the exact bf16 operand and the fp32 queries / probabilities split into bf16 high and low halves
+// (8 heads x {high, low} fill the 16 columns). Softmax statistics are kept online across blocks.
+constexpr int kMlaSub = 64;        // positions per block (four compute waves x 16)
+constexpr int kMlaMaxD = 576;      // latent rank + rotary width
+constexpr int kMlaRowB = kMlaMaxD * 2 + 16;  // LDS row stride of a staged latent (bytes, padded)
+constexpr int kMlaHeads = 8;       // heads per unit: 8 x {high, low} fill the 16 MFMA columns
+struct MlaLds {
+  static constexpr int q = 0;                                  // [18 ks][4 kg][16 col] uint4
+  static constexpr int c = q + (kMlaMaxD / 32) * 4 * 16 * 16;  // [64][kMlaRowB] bf16 latents
+  static constexpr int s = c + kMlaSub * kMlaRowB;             // [64 pos][8 heads] f32 scores
+  static constexpr int p = s + kMlaSub * kMlaHeads * 4;        // [2 kp][4 kg][16 col] uint4
+  static constexpr int st = p + 2 * 4 * 16 * 16;               // m, l, alpha [8 heads] each
+  static constexpr int end = st + 3 * kMlaHeads * 4;
+};
+static_assert(MlaLds::end <= kLdsBytes, "latent attention LDS layout exceeds the workgroup's LDS");
+
+__device__ __forceinline__ uint4 pack_hi_lo(const float (&y)[8], bool lo) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    uint16_t h0 = f2bf(y[e]), h1 = f2bf(y[e + 1]);
+    if (lo) { h0 = f2bf(y[e] - bf2f(h0)); h1 = f2bf(y[e + 1] - bf2f(h1)); }
+    w[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ void mla_phase(CArgs &a, const Phase &ph, char *smem) {
+  const int R = a.R, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rank = ph.rank, rope = ph.rope, D = rank + rope, KS = D / 32, half = rope / 2;
+  const int HG = kMlaHeads, NHG = (ph.heads + HG - 1) / HG;
+  const int CS = ph.chunk, NC = ph.n_chunks;
+  const int nrow = a.verify ? R : 1;             // query rows per sequence
+  const int U = R * NC * NHG;                    // units: (row, chunk, head group)
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int u0 = (int)(((int64_t)U * wg) / G), u1 = (int)(((int64_t)U * (wg + 1)) / G);
+  const float scale = 1.0f / sqrtf((float)(ph.nope + rope));
+  uint4 *Qb = reinterpret_cast<uint4 *>(smem + MlaLds::q);
+  char *Cs = smem + MlaLds::c;
+  float *Sc = reinterpret_cast<float *>(smem + MlaLds::s);
+  uint4 *Pb = reinterpret_cast<uint4 *>(smem + MlaLds::p);
+  float *mst = reinterpret_cast<float *>(smem + MlaLds::st), *lst = mst + kMlaHeads, *alp = lst + kMlaHeads;
+  const float *src = part_of(a, ph.src_part);
+  const float *qt = part_of(a, ph.mla_src);      // absorbed queries [R][heads * rank] (one split)
+  const float2 *rt = reinterpret_cast<const float2 *>(a.rope_mla);
+  uint16_t *cache = reinterpret_cast<uint16_t *>(a.lat[ph.layer]);
+  const int col = lane & 15, kg = lane >> 4;
+  for (int u = u0; u < u1; ++u) {
+    // unit order (head group, row, chunk): the head groups of one (row, chunk) sit G/NHG apart
+    const int hg = u / (R * NC), rc = u - hg * (R * NC), row = rc / NC, c = rc - row * NC;
+    const int seq = a.verify ? 0 : row;
+    const int pbase = pos_of(a, seq);
+    const int prow = pbase + (a.verify ? row : 0);  // this row attends positions 0 .. prow
+    const int j0 = c * CS, j1 = min(j0 + CS, prow + 1);
+    const int h0 = hg * HG;
+    lds_barrier();  // the previous unit's LDS reads are done
+    // ---- queries of the group's heads as the B operand (rotary part rotated at prow) ----
+    for (int it = tid; it < HG * (D / 8); it += kThreads) {
+      const int hl = it / (D / 8), g = it - hl * (D / 8), h = h0 + hl, d0 = g * 8;
+      float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (h < ph.heads) {
+        if (d0 < rank) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = ld_c(qt + (size_t)row * ph.heads * rank + (size_t)h * rank + d0 + e);
+        } else {
+          const int r0 = d0 - rank;  // rotary dims r0..r0+7, partner dims at +-half
+          const int pr = r0 < half ? r0 + half : r0 - half;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float x = 0.0f, xp = 0.0f;
+            for (int s2 = 0; s2 < ph.src_S; ++s2) {
+              const float *pr_row = src + ((size_t)s2 * R + row) * ph.src_N + ph.q_off + h * ph.qk_stride + ph.nope;
+              x += pr_row[r0 + e];
+              xp += pr_row[pr + e];
+            }
+            const int i = (r0 + e) % half;
+            const float2 cs = rt[(size_t)prow * half + i];
+            y[e] = r0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
+          }
+        }
+      }
+      const int ks = g >> 2, kk = g & 3;
+      Qb[(ks * 4 + kk) * 16 + hl] = pack_hi_lo(y, false);
+      Qb[(ks * 4 + kk) * 16 + hl + 8] = pack_hi_lo(y, true);
+    }
+    if (tid < kMlaHeads) { mst[tid] = -INFINITY; lst[tid] = 0.0f; }
+    f32x4 acc[8];
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jb = j0; jb < j1; jb += kMlaSub) {
+      lds_barrier();  // queries staged / the previous block's reads of Cs and Pb are done
+      // ---- stage 64 latent rows (new rows computed from the projections and appended) ----
+      for (int it = tid; it < kMlaSub * (D / 8); it += kThreads) {
+        const int jj = it / (D / 8), g = it - jj * (D / 8), j = jb + jj, d0 = g * 8;
+        uint4 v = uint4{0u, 0u, 0u, 0u};
+        if (j < j1) {
+          if (j < pbase) {
+            v = *reinterpret_cast<const uint4 *>(cache + ((size_t)seq * a.max_ctx + j) * D + d0);
+          } else {  // a row of this step: latent rank part, or the rotated key part, rounded to bf16
+            const int rr = a.verify ? j - pbase : row;
+            float y[8];
+            if (d0 < rank) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                float x = 0.0f;
+                for (int s2 = 0; s2 < ph.src_S; ++s2) x += src[((size_t)s2 * R + rr) * ph.src_N + ph.dkv_off + d0 + e];
+                y[e] = x;
+              }
+            } else {
+              const int r0 = d0 - rank, pr = r0 < half ? r0 + half : r0 - half;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                float x = 0.0f, xp = 0.0f;
+                for (int s2 = 0; s2 < ph.src_S; ++s2) {
+                  const float *kr = src + ((size_t)s2 * R + rr) * ph.src_N + ph.kr_off;
+                  x += kr[r0 + e];
+                  xp += kr[pr + e];
+                }
+                const int i = (r0 + e) % half;
+                const float2 cs = rt[(size_t)j * half + i];
+                y[e] = r0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
+              }
+            }
+            v = pack_hi_lo(y, false);
+            if (hg == 0 && (a.verify ? row == R - 1 : true))  // one unit appends each new row
+              *reinterpret_cast<uint4 *>(cache + ((size_t)seq * a.max_ctx + j) * D + d0) = v;
+          }
+        }
+        *reinterpret_cast<uint4 *>(Cs + jj * kMlaRowB + d0 * 2) = v;
+      }
+      lds_barrier();
+      // ---- scores: wave w takes positions jb + 16 w .. +15 ----
+      if (wave < kCWaves) {
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 av = *reinterpret_cast<const uint4 *>(Cs + (wave * 16 + col) * kMlaRowB + (ks * 32 + kg * 8) * 2);
+          const uint4 bv = Qb[(ks * 4 + kg) * 16 + col];
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), sacc, 0,
+                                                         0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = sacc[e] + __shfl_down(sacc[e], 8);  // high + low columns
+          const int pl = wave * 16 + kg * 4 + e;
+          if (col < 8) Sc[pl * kMlaHeads + col] = (jb + pl < j1) ? v * scale : -INFINITY;
+        }
+      }
+      lds_barrier();
+      // ---- online softmax: 16 lanes per head, 4 positions each ----
+      if (tid < HG * 16) {
+        const int h = tid >> 4, q = tid & 15;
+        float sv[4], bm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = Sc[(q * 4 + e) * kMlaHeads + h];
+          bm = fmaxf(bm, sv[e]);
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
+        const float mo = mst[h], mn = fmaxf(mo, bm);
+        float pv[4], ls = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = mn == -INFINITY ? 0.0f : __expf(sv[e] - mn);
+          ls += pv[e];
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
+        // P as the B operand: positions q*4 .. q*4+3 of head h (two lanes make one group of 8)
+        const float o4[4] = {__shfl_xor(pv[0], 1), __shfl_xor(pv[1], 1), __shfl_xor(pv[2], 1), __shfl_xor(pv[3], 1)};
+        if ((q & 1) == 0) {
+          const float y[8] = {pv[0], pv[1], pv[2], pv[3], o4[0], o4[1], o4[2], o4[3]};
+          const int g = q >> 1, kp = g >> 2, kk = g & 3;
+          Pb[(kp * 4 + kk) * 16 + h] = pack_hi_lo(y, false);
+          Pb[(kp * 4 + kk) * 16 + h + 8] = pack_hi_lo(y, true);
+        }
+        if (q == 0) {
+          const float al = mo == -INFINITY ? 0.0f : __expf(mo - mn);
+          alp[h] = al;
+          mst[h] = mn;
+          lst[h] = lst[h] * al + ls;
+        }
+      }
+      lds_barrier();
+      // ---- out^T += C^T P: wave w takes latent dims 128 w .. +127 (8 row blocks) ----
+      if (wave < kCWaves && wave * 128 < rank) {
+        const float al = alp[col & 7];
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rb][e] *= al;
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const uint4 bv = Pb[(kp * 4 + kg) * 16 + col];
+#pragma unroll
+          for (int rb = 0; rb < 8; ++rb) {
+            const int dim = wave * 128 + rb * 16 + col;
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+              const uint16_t lo16 = *reinterpret_cast<const uint16_t *>(Cs + (kp * 32 + kg * 8 + i) * kMlaRowB + dim * 2);
+              const uint16_t hi16 = *reinterpret_cast<const uint16_t *>(Cs + (kp * 32 + kg * 8 + i + 1) * kMlaRowB + dim * 2);
+              w[i >> 1] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
+            }
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]}),
+                                                              __builtin_bit_cast(bf16x8, bv), acc[rb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    lds_barrier();  // final statistics visible
+    // ---- partials: [row][head][chunk][rank + 2] = (m, l, sum_j p_j c_j) ----
+    const int W = rank + 2;
+    if (wave < kCWaves && wave * 128 < rank) {
+#pragma unroll
+      for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[rb][e] + __shfl_down(acc[rb][e], 8);
+          const int h = h0 + col;
+          if (col < 8 && h < ph.heads) {
+            const int dim = wave * 128 + rb * 16 + kg * 4 + e;
+            st_c(a.attn + (((size_t)row * ph.heads + h) * NC + c) * W + 2 + dim, v);
+          }
+        }
+    }
+    if (tid < HG && h0 + tid < ph.heads) {
+      float *dst = a.attn + (((size_t)row * ph.heads + h0 + tid) * NC + c) * W;
+      st_c(dst, mst[tid]);
+      st_c(dst + 1, lst[tid]);
+    }
+  }
+}
+
+// Log-sum-exp merge of split-KV partials (m, l, sum p v) over chunks, per (row, query head): grouped
+// query attention (head width hd) or latent attention (latent rank).
 __device__ __forceinline__ void merge_phase(CArgs &a, const Phase &ph, char *smem) {
-  const int R = a.R, nq = a.nq, hd = a.hd, NC = ph.n_chunks, W = hd + 2;
+  const bool mla = ph.type == PH_MLA_MERGE;
+  const int R = a.R, nq = mla ? ph.heads : a.nq, hd = mla ? ph.rank : a.hd, NC = ph.n_chunks, W = hd + 2;
   const int U = R * nq;
   const int G = gridDim.x, wg = blockIdx.x, tid = threadIdx.x;
   const int u0 = (int)(((int64_t)U * wg) / G), u1 = (int)(((int64_t)U * (wg + 1)) / G);
@@ -1193,7 +1440,9 @@ __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *sm
       if (a.hd == 64) attn_phase<64>(a, ph, smem);
       else attn_phase<128>(a, ph, smem);
       break;
-    case PH_MERGE: merge_phase(a, ph, smem); break;
+    case PH_MERGE:
+    case PH_MLA_MERGE: merge_phase(a, ph, smem); break;
+    case PH_MLA: mla_phase(a, ph, smem); break;
     case PH_FINAL: final_phase(a, smem); break;
     case PH_HIDDEN_OUT: hidden_out_phase(a); break;
     default: break;
@@ -1349,3 +1598,24 @@ extern "C" __global__ void mk_repack_nvfp4(const uint8_t *__restrict__ codes, co
 }
 
 extern "C" __global__ void mk_store_f32(float *dst, float v) { *dst = v; }
+
+// Per-head transposed repack of the key up-projection W_uk [heads * nope][rank] into the packed matrix
+// [heads * rank][nope]: row h * rank + c, column n holds W_uk[h * nope + n][c], so one product with the
+// per-head query slice gives q~_h = W_uk,h^T q_nope,h.
+extern "C" __global__ void mk_repack_bf16_headT(const uint16_t *__restrict__ src, int64_t heads, int64_t nope, int64_t rank,
+                                                uint4 *__restrict__ dst) {
+  const int64_t KF = nope / 32, rows = heads * rank;
+  const int64_t total = (rows / 16) * KF * 64;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx & 63);
+    const int64_t fr = idx >> 6, t = fr / KF, f = fr % KF;
+    const int64_t r = t * 16 + (lane & 15), h = r / rank, cc = r % rank;
+    const int64_t n0 = f * 32 + 8 * (lane >> 4);
+    uint16_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = src[(h * nope + n0 + i) * rank + cc];
+    dst[(t * KF + f) * 64 + (lane & 15) + 16 * (lane >> 4)] =
+        uint4{(uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+              (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16)};
+  }
+}

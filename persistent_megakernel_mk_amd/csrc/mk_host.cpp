@@ -28,6 +28,7 @@ extern "C" __global__ void mk_repack_bf16(const uint16_t *src, int64_t rows, int
 extern "C" __global__ void mk_repack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
                                            int64_t row_off, int64_t dst_rows);
 extern "C" __global__ void mk_store_f32(float *dst, float v);
+extern "C" __global__ void mk_repack_bf16_headT(const uint16_t *src, int64_t heads, int64_t nope, int64_t rank, uint4 *dst);
 
 namespace {
 
@@ -66,6 +67,9 @@ struct LayerSlots {
   int32_t q_off = 0, k_off = 0, v_off = 0, a_off = 0, b_off = 0;
   // required tensors (kind bitmask) and loaded tensors
   uint32_t need = 0, have = 0;
+  // latent attention: absorbed key up-projection (per-head transposed) and value up-projection
+  Slot wuk_t, wuv;
+  int32_t dkv_off = 0, kr_off = 0;
   // mixture of experts: router, then (routed experts + shared experts) gate|up blocks and down blocks
   Slot router;
   int64_t ex_gu_off = -1, ex_down_off = -1, ex_gu_bytes = 0, ex_down_bytes = 0, ts_off = -1;
@@ -82,6 +86,7 @@ struct Schedule {
   std::vector<Phase> phases;
   int64_t part_floats[3] = {0, 0, 0};
   int32_t n_chunks = 0, chunk = 0;
+  int32_t mla_chunks = 0, mla_chunk = 0;  // latent attention split-KV geometry
 };
 
 }  // namespace
@@ -99,6 +104,7 @@ struct mk_ctx {
   int mix_stride = 0;
   Schedule sched[kMaxRows + 1];  // by row count
   // scratch layout (byte offsets)
+  int64_t o_rope_mla = 0;
   int64_t o_status = 0, o_bar = 0, o_fin = 0, o_x = 0, o_ss = 0, o_part[3] = {0, 0, 0}, o_mix = 0, o_attn = 0,
           o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxRows + 1] = {}, scratch_bytes = 0;
   int64_t kv_bytes = 0, lin_bytes = 0, latent_bytes = 0;
@@ -128,12 +134,12 @@ mk_status validate(const mk_config *c) {
   if (c->max_batch < 1 || c->max_batch > MK_MAX_BATCH) return fail(MK_E_ARG, "max_batch %d out of [1, %d]", c->max_batch, MK_MAX_BATCH);
   if (c->max_ctx < 1) return fail(MK_E_ARG, "max_ctx %d", c->max_ctx);
   if (!(c->eps > 0.0f)) return fail(MK_E_ARG, "eps must be positive");
-  bool any_gqa = false, any_lin = false, any_dense = false, any_moe = false;
+  bool any_gqa = false, any_lin = false, any_dense = false, any_moe = false, any_mla = false;
   for (int l = 0; l < c->n_layers; ++l) {
     int m = c->mixer[l], f = c->ffn_kind[l];
     if (m < MK_MIXER_GQA || m > MK_MIXER_MLA) return fail(MK_E_ARG, "layer %d: bad mixer %d", l, m);
     if (f != MK_FFN_DENSE && f != MK_FFN_MOE) return fail(MK_E_ARG, "layer %d: bad ffn kind %d", l, f);
-    if (m == MK_MIXER_MLA) return fail(MK_E_UNSUPPORTED, "layer %d: latent attention is not built yet", l);
+    any_mla |= m == MK_MIXER_MLA;
     any_gqa |= m == MK_MIXER_GQA;
     any_lin |= m == MK_MIXER_GDN || m == MK_MIXER_KDA;
     any_dense |= f == MK_FFN_DENSE;
@@ -157,6 +163,17 @@ mk_status validate(const mk_config *c) {
     if ((c->n_q_heads * c->head_dim) % 256) return fail(MK_E_UNSUPPORTED, "n_q_heads * head_dim must be a multiple of 256");
     if ((c->n_q_heads / c->n_kv_heads) * kMaxRows > kAttnMaxQ)
       return fail(MK_E_UNSUPPORTED, "query heads per kv head %d exceed %d", c->n_q_heads / c->n_kv_heads, kAttnMaxQ / kMaxRows);
+    if (!(c->rope_theta > 0.0f)) return fail(MK_E_ARG, "rope_theta must be positive");
+  }
+  if (any_mla) {
+    if (c->mla_heads < 1) return fail(MK_E_ARG, "mla_heads %d", c->mla_heads);
+    if (c->kv_rank <= 0 || c->kv_rank % 128 || c->kv_rank + c->rope_dim > 576 || (c->kv_rank + c->rope_dim) % 32)
+      return fail(MK_E_UNSUPPORTED, "latent rank %d (multiple of 128) + rotary width %d must be a multiple of 32 up to 576",
+                  c->kv_rank, c->rope_dim);
+    if (c->rope_dim <= 0 || c->rope_dim % 16) return fail(MK_E_UNSUPPORTED, "rope_dim %d must be a positive multiple of 16", c->rope_dim);
+    if (c->nope_dim <= 0 || c->nope_dim % 128) return fail(MK_E_UNSUPPORTED, "nope_dim %d must be a positive multiple of 128", c->nope_dim);
+    if (c->v_dim <= 0 || c->v_dim % 16 || (c->mla_heads * c->v_dim) % 128)
+      return fail(MK_E_UNSUPPORTED, "v_dim %d: a multiple of 16 with heads * v_dim a multiple of 128", c->v_dim);
     if (!(c->rope_theta > 0.0f)) return fail(MK_E_ARG, "rope_theta must be positive");
   }
   if (any_lin) {
@@ -245,6 +262,22 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
     }
     if (sc.chunk == 0) return fail(MK_E_CAPACITY, "no split-KV chunking fits max_ctx %d", f.max_ctx);
   }
+  // latent attention split-KV: units (row, chunk, 8-head group), chunks a multiple of 64 positions;
+  // fewest positions on the busiest workgroup, then the fewest chunks
+  bool has_mla = false;
+  for (int l = 0; l < f.n_layers; ++l) has_mla |= f.mixer[l] == MK_MIXER_MLA;
+  if (has_mla) {
+    const int nhg = (f.mla_heads + 7) / 8;
+    double best = 1e300;
+    for (int cs = 64; cs <= 64 * ((f.max_ctx + 63) / 64); cs += 64) {
+      const int nc = (f.max_ctx + cs - 1) / cs;
+      const int64_t units = (int64_t)R * nc * nhg;
+      if ((int64_t)nc * (f.kv_rank + 2) * 4 + (nc + 1) * 4 > kLdsBytes) continue;  // merge stages all chunks
+      const double cost = (double)((units + G - 1) / G) * (cs + 64) + 1e-3 * nc;
+      if (cost < best) { best = cost; sc.mla_chunk = cs; sc.mla_chunks = nc; }
+    }
+    if (sc.mla_chunk == 0) return fail(MK_E_CAPACITY, "no latent split-KV chunking fits max_ctx %d", f.max_ctx);
+  }
   Phase e;
   memset(&e, 0, sizeof(e));
   e.type = PH_EMBED;
@@ -274,16 +307,68 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       Phase mg = mx;
       mg.type = PH_MERGE;
       sc.phases.push_back(mg);
+    } else if (m == MK_MIXER_MLA) {
+      // latent attention: absorbed queries (one product per head, its slice of the projection as the
+      // activation), split-KV attention over the latent cache, merge, value up-projection per head
+      const int hq = f.mla_heads, rank = f.kv_rank;
+      Phase ak = gemv_phase(s.wuk_t, ACT_PART, OUT_PART, R, G, 1);
+      ak.layer = l;
+      ak.seg = SEG_HEADS;
+      ak.nseg = hq;
+      ak.seg_T = rank / kTileRows;
+      ak.src_part = 0;
+      ak.src_S = p.S;
+      ak.src_N = p.N;
+      ak.src_off = s.q_off;
+      ak.src_seg = f.nope_dim + f.rope_dim;
+      ak.S = choose_splits(ak.seg_T, hq, ak.KF, R, G, 1, true, false, &ak.pieces);
+      ak.nf = ak.S > 0 ? ak.KF / ak.S : 0;
+      if (mk_status st = add_gemv(ak, 2)) return st;
+      mx.type = PH_MLA;
+      mx.rank = rank;
+      mx.rope = f.rope_dim;
+      mx.nope = f.nope_dim;
+      mx.qk_stride = f.nope_dim + f.rope_dim;
+      mx.dkv_off = s.dkv_off;
+      mx.kr_off = s.kr_off;
+      mx.heads = hq;
+      mx.hgroup = 8;
+      mx.mla_src = 2;
+      mx.chunk = sc.mla_chunk;
+      mx.n_chunks = sc.mla_chunks;
+      sc.phases.push_back(mx);
+      Phase mg = mx;
+      mg.type = PH_MLA_MERGE;
+      sc.phases.push_back(mg);
+      Phase av = gemv_phase(s.wuv, ACT_MIX, OUT_PART, R, G, 64);
+      av.layer = l;
+      av.seg = SEG_HEADS;
+      av.nseg = hq;
+      av.seg_T = f.v_dim / kTileRows;
+      av.src_off = 0;
+      av.src_seg = rank;
+      av.S = choose_splits(av.seg_T, hq, av.KF, R, G, 64, true, false, &av.pieces);
+      av.nf = av.S > 0 ? av.KF / av.S : 0;
+      if (mk_status st = add_gemv(av, 0)) return st;
+      Phase o = gemv_phase(s.wo, ACT_PART, OUT_RESID, R, G, 68);
+      o.layer = l;
+      o.src_part = 0;
+      o.src_S = av.S;
+      o.src_N = av.N;
+      o.cnt_off = (resid++) * (f.hidden / kTileRows);
+      if (mk_status st = add_gemv(o, 1)) return st;
     } else {
       mx.type = PH_DELTA;
       mx.lin_idx = c->lin_index[l];
       mx.per_channel_gate = m == MK_MIXER_KDA;
       sc.phases.push_back(mx);
     }
-    Phase o = gemv_phase(s.wo, ACT_MIX, OUT_RESID, R, G, 68);
-    o.layer = l;
-    o.cnt_off = (resid++) * (f.hidden / kTileRows);
-    if (mk_status st = add_gemv(o, 1)) return st;
+    if (m != MK_MIXER_MLA) {
+      Phase o = gemv_phase(s.wo, ACT_MIX, OUT_RESID, R, G, 68);
+      o.layer = l;
+      o.cnt_off = (resid++) * (f.hidden / kTileRows);
+      if (mk_status st = add_gemv(o, 1)) return st;
+    }
     if (f.ffn_kind[l] == MK_FFN_DENSE) {
       Phase gu = gemv_phase(s.gu, ACT_NORM, OUT_PART, R, G, 64);
       gu.layer = l;
@@ -416,6 +501,16 @@ mk_status layout(mk_ctx *c) {
       rows = s.v_off + f.n_kv_heads * f.head_dim;
       inner = f.n_q_heads * f.head_dim;
       s.need = kind_bit(MK_W_Q) | kind_bit(MK_W_K) | kind_bit(MK_W_V) | kind_bit(MK_W_O);
+    } else if (m == MK_MIXER_MLA) {
+      const int hq = f.mla_heads, qk = f.nope_dim + f.rope_dim;
+      s.q_off = 0;
+      s.dkv_off = (int)round16((int64_t)hq * qk);
+      s.kr_off = s.dkv_off + f.kv_rank;
+      rows = (int)round16(s.kr_off + f.rope_dim);
+      inner = hq * f.v_dim;
+      mix_w = std::max(mix_w, hq * f.kv_rank);  // merged latent outputs
+      s.need = kind_bit(MK_W_Q) | kind_bit(MK_W_DKV) | kind_bit(MK_W_KR) | kind_bit(MK_W_UK) | kind_bit(MK_W_UV) |
+               kind_bit(MK_W_O);
     } else {
       const int hk = f.lin_heads * f.d_k;
       s.q_off = 0;
@@ -432,6 +527,10 @@ mk_status layout(mk_ctx *c) {
     s.need |= kind_bit(MK_W_ATTN_NORM) | kind_bit(MK_W_FFN_NORM);
     mix_w = std::max(mix_w, inner);
     place(s.mix_in, rows, H, true);
+    if (m == MK_MIXER_MLA) {
+      place(s.wuk_t, f.mla_heads * f.kv_rank, f.nope_dim, true);
+      place(s.wuv, f.mla_heads * f.v_dim, f.kv_rank, true);
+    }
     place(s.wo, H, inner, true);
     if (f.ffn_kind[l] == MK_FFN_DENSE) {
       s.need |= kind_bit(MK_W_GATE) | kind_bit(MK_W_UP) | kind_bit(MK_W_DOWN);
@@ -477,6 +576,7 @@ mk_status scratch_layout(mk_ctx *c) {
     if (s.phases.empty()) continue;
     for (int i = 0; i < 3; ++i) part[i] = std::max<int64_t>(part[i], s.part_floats[i]);
     if (f.n_q_heads > 0) attn = std::max<int64_t>(attn, (int64_t)r * f.n_q_heads * s.n_chunks * (f.head_dim + 2));
+    if (s.mla_chunks > 0) attn = std::max<int64_t>(attn, (int64_t)r * f.mla_heads * s.mla_chunks * (f.kv_rank + 2));
   }
   c->o_status = take(256);
   c->o_bar = take(9 * 128);
@@ -489,7 +589,8 @@ mk_status scratch_layout(mk_ctx *c) {
   c->o_cand = take((int64_t)G * R * 2 * 4);
   c->o_rope = take(f.n_q_heads > 0 ? (int64_t)f.max_ctx * (f.head_dim / 2) * 2 * 4 : 0);
   c->o_snap = take(f.vocab > 0 ? (int64_t)c->n_lin * kMaxRows * f.lin_heads * f.d_v * f.d_k * 4 : 0);
-  c->o_ptrs = take((int64_t)(3 * MK_MAX_LAYERS + MK_MAX_LAYERS) * 8);
+  c->o_rope_mla = take(f.mla_heads > 0 ? (int64_t)f.max_ctx * (f.rope_dim / 2) * 2 * 4 : 0);
+  c->o_ptrs = take((int64_t)5 * MK_MAX_LAYERS * 8);
   for (int r = 1; r <= kMaxRows; ++r)
     if (!c->sched[r].phases.empty()) c->o_phases[r] = take((int64_t)c->sched[r].phases.size() * sizeof(Phase));
   c->scratch_bytes = off;
@@ -560,13 +661,32 @@ mk_status resolve(mk_ctx *c, const mk_weight_desc &w, Slot **slot, int64_t *row_
     case MK_W_FFN_NORM: *slot = &s.ffn_norm; *rows = 1; *cols = H; return MK_OK;
     case MK_W_Q:
       *slot = &s.mix_in; *row_off = s.q_off; *cols = H;
-      *rows = lin ? (int64_t)f.lin_heads * f.d_k : (int64_t)f.n_q_heads * f.head_dim;
+      *rows = m == MK_MIXER_MLA ? (int64_t)f.mla_heads * (f.nope_dim + f.rope_dim)
+                                : lin ? (int64_t)f.lin_heads * f.d_k : (int64_t)f.n_q_heads * f.head_dim;
+      return MK_OK;
+    case MK_W_DKV:
+      if (m != MK_MIXER_MLA) break;
+      *slot = &s.mix_in; *row_off = s.dkv_off; *rows = f.kv_rank; *cols = H;
+      return MK_OK;
+    case MK_W_KR:
+      if (m != MK_MIXER_MLA) break;
+      *slot = &s.mix_in; *row_off = s.kr_off; *rows = f.rope_dim; *cols = H;
+      return MK_OK;
+    case MK_W_UK:  // natural [heads * nope][rank]; stored per-head transposed
+      if (m != MK_MIXER_MLA) break;
+      *slot = &s.wuk_t; *rows = (int64_t)f.mla_heads * f.nope_dim; *cols = f.kv_rank;
+      return MK_OK;
+    case MK_W_UV:
+      if (m != MK_MIXER_MLA) break;
+      *slot = &s.wuv; *rows = (int64_t)f.mla_heads * f.v_dim; *cols = f.kv_rank;
       return MK_OK;
     case MK_W_K:
+      if (m == MK_MIXER_MLA) break;
       *slot = &s.mix_in; *row_off = s.k_off; *cols = H;
       *rows = lin ? (int64_t)f.lin_heads * f.d_k : (int64_t)f.n_kv_heads * f.head_dim;
       return MK_OK;
     case MK_W_V:
+      if (m == MK_MIXER_MLA) break;
       *slot = &s.mix_in; *row_off = s.v_off; *cols = H;
       *rows = lin ? (int64_t)f.lin_heads * f.d_v : (int64_t)f.n_kv_heads * f.head_dim;
       return MK_OK;
@@ -627,6 +747,8 @@ void fill_args(mk_ctx *c, StepArgs &a, int R, int verify, const mk_step_io *io) 
   a.vc = ptrs + MK_MAX_LAYERS;
   a.ls = ptrs + 2 * MK_MAX_LAYERS;
   a.lsl = ptrs + 3 * MK_MAX_LAYERS;
+  a.lat = ptrs + 4 * MK_MAX_LAYERS;
+  a.rope_mla = reinterpret_cast<const float *>(c->scratch + c->o_rope_mla);
   a.tokens = io->tokens;
   a.hidden_in = io->hidden_in;
   const int nseq = verify ? 1 : R;
@@ -776,6 +898,8 @@ mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
     const int m = f.mixer[l];
     if (m == MK_MIXER_GQA && (!b->k_cache[l] || !b->v_cache[l])) return fail(MK_E_ARG, "layer %d: K/V cache missing", l);
     if ((m == MK_MIXER_GDN || m == MK_MIXER_KDA) && !b->lin_state[l]) return fail(MK_E_ARG, "layer %d: state missing", l);
+    if (m == MK_MIXER_MLA && (!b->latent[l] || ((uintptr_t)b->latent[l] & 15)))
+      return fail(MK_E_ARG, "layer %d: latent cache missing or not 16-byte aligned", l);
   }
   HIP_TRY(hipSetDevice(c->device));
   c->bufs = *b;
@@ -784,8 +908,9 @@ mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
   HIP_TRY(hipMemset(c->wbuf, 0, (size_t)c->packed_bytes));  // padding rows of fused matrices are zero
   HIP_TRY(hipMemset(c->scratch, 0, (size_t)c->scratch_bytes));
   // per-layer state pointers
-  std::vector<void *> ptrs(4 * MK_MAX_LAYERS, nullptr);
+  std::vector<void *> ptrs(5 * MK_MAX_LAYERS, nullptr);
   for (int l = 0; l < f.n_layers; ++l) {
+    ptrs[4 * MK_MAX_LAYERS + l] = b->latent[l];
     ptrs[l] = b->k_cache[l];
     ptrs[MK_MAX_LAYERS + l] = b->v_cache[l];
     ptrs[2 * MK_MAX_LAYERS + l] = b->lin_state[l];
@@ -803,6 +928,18 @@ mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
         rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
       }
     HIP_TRY(hipMemcpy(c->scratch + c->o_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
+  }
+  // rotary table of the latent attention's rotary part (width rope_dim), same convention
+  if (f.mla_heads > 0) {
+    const int half = f.rope_dim / 2;
+    std::vector<float> rope((size_t)f.max_ctx * half * 2);
+    for (int p = 0; p < f.max_ctx; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * std::pow((double)f.rope_theta, -2.0 * i / (double)f.rope_dim);
+        rope[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+        rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    HIP_TRY(hipMemcpy(c->scratch + c->o_rope_mla, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
   }
   for (int r = 1; r <= kMaxRows; ++r) {
     const Schedule &s = c->sched[r];
@@ -872,7 +1009,14 @@ mk_status mk_load_weights(mk_ctx *c, const mk_weight_desc *w, int n, void *strea
       *tg.have_flag = 1;
       continue;
     }
-    if (!slot->packed) {
+    if (w[i].kind == MK_W_UK) {
+      const mk_config &f = c->cfg;
+      const int64_t total = ((int64_t)f.mla_heads * f.kv_rank / 16) * (f.nope_dim / kFragK) * 64;
+      const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+      hipLaunchKernelGGL(mk_repack_bf16_headT, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(w[i].data),
+                         (int64_t)f.mla_heads, (int64_t)f.nope_dim, (int64_t)f.kv_rank, reinterpret_cast<uint4 *>(c->wbuf + slot->off));
+      HIP_TRY(hipGetLastError());
+    } else if (!slot->packed) {
       HIP_TRY(hipMemcpyAsync(c->wbuf + slot->off, w[i].data, (size_t)rows * cols * 2, hipMemcpyDeviceToDevice, st));
     } else {
       const int64_t KF = cols / kFragK;

@@ -123,7 +123,7 @@ struct StepArgs {
   float *part[3];      // partial sums [S][R][N]
   float *mix;          // mixer outputs [R][M]
   float *attn;         // split-KV partials [R][nq][n_chunks][hd + 2] (latent: [R][heads][n_chunks][rank + 2])
-  float *rope_mla;     // [max_ctx][rope/2][2] cos, sin for the latent attention's rotary part
+  const float *rope_mla;  // [max_ctx][rope/2][2] cos, sin for the latent attention's rotary part
   void *const *lat;    // per layer latent caches
   float *cand;         // argmax candidates [G][R][2]
   const float *rope;   // [max_ctx][hd/2][2] cos, sin

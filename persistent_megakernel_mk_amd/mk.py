@@ -172,6 +172,7 @@ class Megakernel:
         self.k_cache: Dict[int, "torch.Tensor"] = {}
         self.v_cache: Dict[int, "torch.Tensor"] = {}
         self.lin_state: Dict[int, "torch.Tensor"] = {}
+        self.latent: Dict[int, "torch.Tensor"] = {}
         B = self.max_batch
         b = Buffers()
         b.packed_weights = self.wbuf.data_ptr()
@@ -187,6 +188,10 @@ class Megakernel:
             elif m in ("gdn", "kda"):
                 self.lin_state[l] = torch.zeros((B, cfg.lin_heads, cfg.d_v, cfg.d_k), dtype=torch.float32, device=dev)
                 b.lin_state[l] = self.lin_state[l].data_ptr()
+            elif m == "mla":
+                shp = (B, cfg.max_ctx, cfg.kv_rank + cfg.rope_dim)
+                self.latent[l] = torch.zeros(shp, dtype=torch.bfloat16, device=dev)
+                b.latent[l] = self.latent[l].data_ptr()
         check(self.lib.mk_bind_buffers(self.ctx, ctypes.byref(b)))
         self._bufs = b
 
@@ -247,6 +252,8 @@ class Megakernel:
                 dst = self.v_cache[layer]
             elif kind == "lstate":
                 dst = self.lin_state[layer]
+            elif kind == "latent":
+                dst = self.latent[layer]
             else:
                 raise KeyError(name)
             src = torch.from_numpy(np.ascontiguousarray(a))
@@ -263,6 +270,8 @@ class Megakernel:
             out[f"l{l}.vcache"] = self.v_cache[l][:B].view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)
         for l, t in self.lin_state.items():
             out[f"l{l}.lstate"] = t[:B].cpu().numpy()
+        for l, t in self.latent.items():
+            out[f"l{l}.latent"] = t[:B].view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)
         return out
 
     # ---- steps ----------------------------------------------------------------------------

@@ -118,6 +118,9 @@ _reg(ModelConfig(name="c3s", n_layers=4, hidden=1024, vocab=0, mixers=_pattern(4
 # variants that isolate one part of the path: Kimi delta attention with dense FFNs, and the NVFP4
 # mixture-of-experts slice with bf16 experts
 _reg(replace(CONFIGS["c1s"], name="c1s_kda", mixers=_pattern(4, 4, "gqa", "kda"), seed=2005))
+# latent attention with dense FFNs and a vocabulary (decode and verify)
+_reg(replace(CONFIGS["c1s"], name="c1s_mla", mixers=_pattern(4, 4, "mla", "gdn"), mla_heads=12, kv_rank=256,
+             rope_dim=64, nope_dim=128, v_dim=64, seed=2007))
 _reg(ModelConfig(name="c4s", n_layers=2, hidden=1024, vocab=0, mixers=("gqa",) * 2, ffns=("moe",) * 2,
                  n_q_heads=8, n_kv_heads=2, head_dim=128, n_experts=16, top_k=4, expert_ffn=512, n_shared=1,
                  expert_format="nvfp4", ctx=160, batch=4, seed=2004))

@@ -64,9 +64,11 @@ def compare_states(gpu_S, ref_S, new_positions=None):
         diff = np.abs(gf - rf)
         assert np.all(diff <= bound), (name, float(diff.max()))
         if new_positions is not None:
-            mask = np.ones(g.shape[2], bool)
+            pax = 1 if name.endswith("latent") else 2  # position axis: latent [B][pos][D], K/V [B][heads][pos][d]
+            mask = np.ones(g.shape[pax], bool)
             mask[list(new_positions)] = False
-            assert np.array_equal(g[:, :, mask], ref[:, :, mask]), name
+            idx = (slice(None),) * pax + (mask,)
+            assert np.array_equal(g[idx], ref[idx]), name
 
 
 def assert_routes(gpu_idx, gpu_w, route_log, moe_layers, tol_rel=REL_TOL):

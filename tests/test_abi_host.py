@@ -127,3 +127,25 @@ def test_expert_weight_validation(mkmod, synth):
     assert mkmod.weight_target("l0.router") == (0, mkmod.W_ROUTER, -1)
     d = mkmod.WeightDesc()
     assert h.lib.mk_load_weights(h.ctx, ctypes.byref(d), 1, None) == 3  # MK_E_UNSUPPORTED: host-only
+
+
+def test_mla_schedule(mkmod, synth):
+    """Latent attention layers: fused q / latent / rotary-key product, absorbed-query product (one segment
+    per head), split-KV latent attention, merge, value up-projection (one segment per head), output
+    product; the chunking covers the cache and gives at most one unit per workgroup at batch 8 (C3)."""
+    cfg = synth.CONFIGS["c3"]
+    h = mkmod.HostContext(cfg, max_batch=8)
+    ph = h.phases(8)
+    l = cfg.mixers.index("mla")
+    first = 1 + l * 7  # embed, then 7 phases per KDA+MoE layer before it
+    types = [p[0] for p in ph[first:first + 6]]
+    assert types == [2, 2, 8, 9, 2, 2]
+    qkv, ak, att, mg, av, o = ph[first:first + 6]
+    hq, rank = cfg.mla_heads, cfg.kv_rank
+    assert qkv[2] >= hq * (cfg.nope_dim + cfg.rope_dim) + rank + cfg.rope_dim
+    assert ak[2] == hq * rank and ak[3] == cfg.nope_dim and ak[6] == 1  # complete absorbed queries
+    assert av[2] == hq * cfg.v_dim and av[3] == rank
+    assert o[2] == cfg.hidden and o[3] == hq * cfg.v_dim and o[9] == 1
+    n_chunks, chunk = att[12], att[13]
+    assert chunk % 64 == 0 and n_chunks * chunk >= cfg.max_ctx > (n_chunks - 1) * chunk
+    assert 8 * n_chunks * (hq // 8) <= h.sizes.n_workgroups
