@@ -137,7 +137,7 @@ def test_mla_schedule(mkmod, synth):
     h = mkmod.HostContext(cfg, max_batch=8)
     ph = h.phases(8)
     l = cfg.mixers.index("mla")
-    first = 1 + l * 7  # embed, then 7 phases per KDA+MoE layer before it
+    first = 1 + l * 6  # embed, then 6 phases per KDA+MoE layer before it
     types = [p[0] for p in ph[first:first + 6]]
     assert types == [2, 2, 8, 9, 2, 2]
     qkv, ak, att, mg, av, o = ph[first:first + 6]
