@@ -852,61 +852,113 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
 }
 
 // ---------------------------------------------------------------------------------------------
-// gated delta rule: per (sequence, head, 16 state rows); one wave per state row, 2 channels per lane
+// gated delta rule: per (sequence, head, block of RPU state rows)
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph) {
-  constexpr int kRowsPerUnit = 16;
+// Per unit the head's normalised query and key, decay gate(s), write strength and the block's values
+// are formed once (all five waves, one vector per wave task) into LDS while the block's state rows are
+// already loading; then each compute wave advances RPU/4 state rows (two key channels per lane): with
+// a the decay of each channel, S_r <- a * S_r; u = S_r . k; S_r <- S_r + beta (v_r - u) k; o_r = S_r . q.
+// A verify block advances each state row through its 8 token rows in order and records every
+// intermediate row (the snapshots the commit selects from).
+constexpr int kDeltaMaxRpw = 4;  // state rows per compute wave and unit
+__device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, Hl = a.lin_heads, dk = a.dk, dv = a.dv;
-  const int RB = dv / kRowsPerUnit;
+  const int RPU = ph.chunk, RPW = RPU / kCWaves;  // state rows per unit / per compute wave
+  const int RB = dv / RPU;
   const int nseq = a.verify ? 1 : R;
+  const int nj = a.verify ? R : 1;  // token rows applied to each state row, in order
   const int U = nseq * Hl * RB;
   const int G = gridDim.x, wg = blockIdx.x;
   const int u0 = (int)(((int64_t)U * wg) / G), u1 = (int)(((int64_t)U * (wg + 1)) / G);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const float *src = part_of(a, ph.src_part);
+  float *qh = reinterpret_cast<float *>(smem);  // [nj][dk]
+  float *kh = qh + kMaxRows * 128;              // [nj][dk]
+  float *al = kh + kMaxRows * 128;              // [nj][dk] decay per key channel
+  float *be = al + kMaxRows * 128;              // [nj] write strength
+  float *vv = be + kMaxRows;                    // [nj][RPU] values of the block's rows
   const int c0 = lane * 2;
   for (int u = u0; u < u1; ++u) {
     const int b = u / (Hl * RB), h = (u / RB) % Hl, rb = u % RB;
-    for (int r = rb * kRowsPerUnit + wave; r < (rb + 1) * kRowsPerUnit; r += kWavesTotal) {
-      float *Srow = reinterpret_cast<float *>(a.ls[ph.layer]) + (((size_t)b * Hl + h) * dv + r) * dk;
-      float2 S = *reinterpret_cast<const float2 *>(Srow + c0);
-      const int j0 = a.verify ? 0 : b, j1 = a.verify ? a.R : b + 1;
-      for (int j = j0; j < j1; ++j) {
-        float q0 = 0, q1 = 0, k0 = 0, k1 = 0, vr = 0, av0 = 0, av1 = 0, bv = 0;
-        for (int s2 = 0; s2 < ph.src_S; ++s2) {
-          const float *row = src + ((size_t)s2 * R + j) * ph.src_N;
-          const float2 qq = *reinterpret_cast<const float2 *>(row + ph.q_off + h * dk + c0);
-          const float2 kk = *reinterpret_cast<const float2 *>(row + ph.k_off + h * dk + c0);
-          q0 += qq.x; q1 += qq.y; k0 += kk.x; k1 += kk.y;
-          vr += row[ph.v_off + h * dv + r];
-          if (ph.per_channel_gate) {
-            const float2 aa = *reinterpret_cast<const float2 *>(row + ph.a_off + h * dk + c0);
-            av0 += aa.x; av1 += aa.y;
-          } else {
-            av0 += row[ph.a_off + h];
-          }
-          bv += row[ph.b_off + h];
-        }
-        if (!ph.per_channel_gate) av1 = av0;
-        const float qn = 1.0f / sqrtf(wave_sum(q0 * q0 + q1 * q1) + 1e-6f);
-        const float kn = 1.0f / sqrtf(wave_sum(k0 * k0 + k1 * k1) + 1e-6f);
-        q0 *= qn; q1 *= qn; k0 *= kn; k1 *= kn;
-        const float al0 = __expf(-softplusf_(av0)), al1 = ph.per_channel_gate ? __expf(-softplusf_(av1)) : al0;
-        const float beta = sigmoidf_(bv);
-        S.x *= al0; S.y *= al1;
-        const float uu = wave_sum(S.x * k0 + S.y * k1);
-        const float delta = beta * (vr - uu);
-        S.x += delta * k0; S.y += delta * k1;
-        const float o = wave_sum(S.x * q0 + S.y * q1);
-        if (lane == 0) st_c(a.mix + (size_t)j * a.mix_stride + h * dv + r, o);
-        if (a.verify) {
-          float *sn = a.snap + ((((size_t)ph.lin_idx * kMaxRows + j) * Hl + h) * dv + r) * dk + c0;
-          st_c(sn, S.x);
-          st_c(sn + 1, S.y);
-        }
+    // this wave's state rows start loading before the gates are formed
+    float2 S[kDeltaMaxRpw];
+    float *Srow[kDeltaMaxRpw];
+#pragma unroll
+    for (int i = 0; i < kDeltaMaxRpw; ++i) {
+      Srow[i] = nullptr;
+      if (wave < kCWaves && i < RPW) {
+        const int r = rb * RPU + wave * RPW + i;
+        Srow[i] = reinterpret_cast<float *>(a.ls[ph.layer]) + (((size_t)b * Hl + h) * dv + r) * dk;
+        S[i] = *reinterpret_cast<const float2 *>(Srow[i] + c0);
       }
-      if (!a.verify) *reinterpret_cast<float2 *>(Srow + c0) = S;
     }
+    // gates and vectors: task t = (token row j, kind) for kinds q, k, decay + strength + values
+    for (int t = wave; t < 3 * nj; t += kWavesTotal) {
+      const int j = t / 3, kind = t - j * 3;
+      const int row = a.verify ? j : b;
+      if (kind < 2) {
+        const int off = (kind == 0 ? ph.q_off : ph.k_off) + h * dk + c0;
+        float x0 = 0.0f, x1 = 0.0f;
+        for (int s2 = 0; s2 < ph.src_S; ++s2) {
+          const float2 p2 = *reinterpret_cast<const float2 *>(src + ((size_t)s2 * R + row) * ph.src_N + off);
+          x0 += p2.x;
+          x1 += p2.y;
+        }
+        const float n = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) + 1e-6f);
+        float *dst = (kind == 0 ? qh : kh) + j * 128 + c0;
+        dst[0] = x0 * n;
+        dst[1] = x1 * n;
+      } else {
+        float a0 = 0.0f, a1 = 0.0f, bb = 0.0f, vr = 0.0f;
+        for (int s2 = 0; s2 < ph.src_S; ++s2) {
+          const float *pr = src + ((size_t)s2 * R + row) * ph.src_N;
+          if (ph.per_channel_gate) {
+            const float2 p2 = *reinterpret_cast<const float2 *>(pr + ph.a_off + h * dk + c0);
+            a0 += p2.x;
+            a1 += p2.y;
+          } else {
+            a0 += pr[ph.a_off + h];
+          }
+          bb += pr[ph.b_off + h];
+          if (lane < RPU) vr += pr[ph.v_off + h * dv + rb * RPU + lane];
+        }
+        if (!ph.per_channel_gate) a1 = a0;
+        al[j * 128 + c0] = __expf(-softplusf_(a0));
+        al[j * 128 + c0 + 1] = ph.per_channel_gate ? __expf(-softplusf_(a1)) : al[j * 128 + c0];
+        if (lane == 0) be[j] = sigmoidf_(bb);
+        if (lane < RPU) vv[j * RPU + lane] = vr;
+      }
+    }
+    lds_barrier();
+    if (wave < kCWaves) {
+#pragma unroll
+      for (int i = 0; i < kDeltaMaxRpw; ++i) {
+        if (i >= RPW) break;
+        const int rl = wave * RPW + i, r = rb * RPU + rl;
+        float2 st = S[i];
+        for (int j = 0; j < nj; ++j) {
+          const float2 q2 = *reinterpret_cast<const float2 *>(qh + j * 128 + c0);
+          const float2 k2 = *reinterpret_cast<const float2 *>(kh + j * 128 + c0);
+          const float2 a2 = *reinterpret_cast<const float2 *>(al + j * 128 + c0);
+          st.x *= a2.x;
+          st.y *= a2.y;
+          const float uu = wave_sum(st.x * k2.x + st.y * k2.y);
+          const float delta = be[j] * (vv[j * RPU + rl] - uu);
+          st.x += delta * k2.x;
+          st.y += delta * k2.y;
+          const float o = wave_sum(st.x * q2.x + st.y * q2.y);
+          const int orow = a.verify ? j : b;
+          if (lane == 0) st_c(a.mix + (size_t)orow * a.mix_stride + h * dv + r, o);
+          if (a.verify) {
+            float *sn = a.snap + ((((size_t)ph.lin_idx * kMaxRows + j) * Hl + h) * dv + r) * dk + c0;
+            st_c(sn, st.x);
+            st_c(sn + 1, st.y);
+          }
+        }
+        if (!a.verify) *reinterpret_cast<float2 *>(Srow[i] + c0) = st;
+      }
+    }
+    lds_barrier();  // LDS gates are reused by the next unit
   }
 }
 
@@ -1435,7 +1487,7 @@ using namespace mk;
 __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *smem) {
   switch (ph.type) {
     case PH_EMBED: embed_phase(a, ph, smem); break;
-    case PH_DELTA: delta_phase(a, ph); break;
+    case PH_DELTA: delta_phase(a, ph, smem); break;
     case PH_ATTN:
       if (a.hd == 64) attn_phase<64>(a, ph, smem);
       else attn_phase<128>(a, ph, smem);
@@ -1459,7 +1511,7 @@ __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *sm
 // stores cross-workgroup results and runs the grid barrier. The two kinds of wave run separate copies
 // of the phase loop with the same sequence of workgroup barriers, so the weight ring is not live in
 // the sync wave's code.
-template <bool HAS_FP4>
+template <bool HAS_FP4, int RING>
 __device__ __forceinline__ void step_body(char *smem) {
   CArgs *ap = (CArgs *)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ int abort_flag;
@@ -1492,8 +1544,8 @@ __device__ __forceinline__ void step_body(char *smem) {
       if (abort_flag) return;
     }
   } else {
-    uint4 ring[kRing];
-    uint32_t sring[kRing];
+    uint4 ring[RING];
+    uint32_t sring[RING];
     Stream st;
     int head = 0;
     st.route_q = -1;
@@ -1503,7 +1555,7 @@ __device__ __forceinline__ void step_body(char *smem) {
       while (q < a.phase_end && cphase(a, q)->type != PH_GEMV) ++q;
       stream_seek(st, a, smem, wave, q < a.phase_end ? q : -1);
 #pragma unroll
-      for (int d = 0; d < kRing; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
+      for (int d = 0; d < RING; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
     }
     for (int p = ap->phase_begin; p < ap->phase_end; ++p) {
       CArgs &a = *ap;
@@ -1517,10 +1569,10 @@ __device__ __forceinline__ void step_body(char *smem) {
           st.route_q = route_q;
           stream_seek(st, a, smem, wave, p);
 #pragma unroll
-          for (int d = 0; d < kRing; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
+          for (int d = 0; d < RING; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
           head = 0;
         }
-        gemv_compute<HAS_FP4, kRing>(a, ph, smem, ring, sring, st, head);
+        gemv_compute<HAS_FP4, RING>(a, ph, smem, ring, sring, st, head);
       } else {
         common_phase(a, ph, smem);
       }
@@ -1535,13 +1587,13 @@ __device__ __forceinline__ void step_body(char *smem) {
 extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel(StepArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   (void)args;
-  step_body<false>(smem);
+  step_body<false, kRing>(smem);
 }
 
 extern "C" __global__ void __launch_bounds__(kThreads) mk_step_kernel_nvfp4(StepArgs args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   (void)args;
-  step_body<true>(smem);
+  step_body<true, kRingNvfp4>(smem);
 }
 
 // Weight repacking: natural bf16 [rows][cols] -> tile-major MFMA fragments. Fragment (t, f) holds, for

@@ -361,6 +361,8 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       mx.type = PH_DELTA;
       mx.lin_idx = c->lin_index[l];
       mx.per_channel_gate = m == MK_MIXER_KDA;
+      // state rows per unit: 8 while that gives at most one unit per workgroup, else 16
+      mx.chunk = (int64_t)(R) * f.lin_heads * (f.d_v / 8) <= G ? 8 : 16;
       sc.phases.push_back(mx);
     }
     if (m != MK_MIXER_MLA) {

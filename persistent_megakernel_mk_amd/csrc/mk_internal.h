@@ -10,7 +10,8 @@ constexpr int kSyncWave = kCWaves;        // index of the sync wave (reductions,
 constexpr int kWavesTotal = kCWaves + 1;
 constexpr int kThreads = kWavesTotal * 64;  // threads per workgroup
 constexpr int kCThreads = kCWaves * 64;     // threads of the compute waves
-constexpr int kRing = 12;                 // weight fragments in flight per compute wave (12 KiB)
+constexpr int kRing = 12;                 // weight items in flight per compute wave (12 KiB), bf16 build
+constexpr int kRingNvfp4 = 12;            // the same for the build that also streams NVFP4 items
 constexpr int kTileRows = 16;             // weight rows per MFMA tile
 constexpr int kFragK = 32;                // reduction columns per 1 KiB weight fragment
 constexpr int kLdsBytes = 160 * 1024 - 512;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU, minus static)
