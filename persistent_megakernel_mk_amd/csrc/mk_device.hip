@@ -962,144 +962,224 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
   }
 }
 
+// bf16 high part (or low part: value minus high part) of eight fp32 values, packed
+__device__ __forceinline__ uint4 pack_hi_lo(const float (&y)[8], bool lo) {
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    uint16_t h0 = f2bf(y[e]), h1 = f2bf(y[e + 1]);
+    if (lo) { h0 = f2bf(y[e] - bf2f(h0)); h1 = f2bf(y[e + 1] - bf2f(h1)); }
+    w[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
 // ---------------------------------------------------------------------------------------------
-// split-KV grouped-query attention: per (sequence, kv head, chunk of positions)
+// split-KV grouped-query attention: per (query row, kv head, chunk of positions)
 // ---------------------------------------------------------------------------------------------
+// The query heads of one kv head (at most 8) take the 16 MFMA columns as bf16 high/low halves; per
+// 64-position block the scores K (64 x d) * Q^T and the readout V^T (d x 64) * P run on
+// v_mfma_f32_16x16x32_bf16 with the cached bf16 K/V rows as exact operands, softmax statistics kept
+// online across blocks; the block's new rows (this step's tokens) are rotated, rounded to bf16 and
+// appended. Partials (m, l, sum p v) per (row, query head, chunk) go to the merge phase.
+constexpr int kGqaSub = 64;
+template <int HD>
+struct GqaLds {
+  static constexpr int rowb = HD * 2 + 16;                  // padded LDS row of a staged K or V row (bytes)
+  static constexpr int q = 0;                               // [HD/32 ks][4 kg][16 col] uint4
+  static constexpr int k = q + (HD / 32) * 4 * 16 * 16;     // [64][rowb]
+  static constexpr int v = k + kGqaSub * rowb;              // [64][rowb]
+  static constexpr int s = v + kGqaSub * rowb;              // [64][8] f32 scores
+  static constexpr int p = s + kGqaSub * 8 * 4;             // [2 kp][4 kg][16 col] uint4
+  static constexpr int st = p + 2 * 4 * 16 * 16;            // m, l, alpha [8]
+};
+
 template <int HD>
 __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem) {
+  typedef GqaLds<HD> L;
   const int R = a.R, nq = a.nq, nkv = a.nkv, grp = nq / nkv;
   const int CS = ph.chunk, NC = ph.n_chunks;
-  const int nseq = a.verify ? 1 : R;
-  const int nrow = a.verify ? R : 1;  // query rows per unit
-  const int Q = grp * nrow;
-  const int U = nseq * nkv * NC;
-  const int G = gridDim.x, wg = blockIdx.x, tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int U = R * nkv * NC;  // units: (row, kv head, chunk)
+  const int G = gridDim.x, wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u0 = (int)(((int64_t)U * wg) / G), u1 = (int)(((int64_t)U * (wg + 1)) / G);
   const float scale = 1.0f / sqrtf((float)HD);
-  constexpr int half = HD / 2;
-  float *qs = reinterpret_cast<float *>(smem);                        // [Q][HD]       <= 32 KiB
-  uint16_t *Ks = reinterpret_cast<uint16_t *>(qs + kAttnMaxQ * 128);  // [CS][HD] bf16 <= 32 KiB
-  uint16_t *Vs = Ks + kAttnMaxChunk * 128;                            // [CS][HD] bf16 <= 32 KiB
-  float *sc = reinterpret_cast<float *>(Vs + kAttnMaxChunk * 128);    // [Q][CS]       <= 32 KiB
-  float *ml = sc + kAttnMaxQ * kAttnMaxChunk;                         // [Q][2]
-  int *rpos = reinterpret_cast<int *>(ml + kAttnMaxQ * 2);            // [nrow]
+  constexpr int half = HD / 2, KS = HD / 32;
+  uint4 *Qb = reinterpret_cast<uint4 *>(smem + L::q);
+  char *Ks = smem + L::k, *Vs = smem + L::v;
+  float *Sc = reinterpret_cast<float *>(smem + L::s);
+  uint4 *Pb = reinterpret_cast<uint4 *>(smem + L::p);
+  float *mst = reinterpret_cast<float *>(smem + L::st), *lst = mst + 8, *alp = lst + 8;
   const float *src = part_of(a, ph.src_part);
   uint16_t *kc = reinterpret_cast<uint16_t *>(a.kc[ph.layer]);
   uint16_t *vc = reinterpret_cast<uint16_t *>(a.vc[ph.layer]);
-
+  const float2 *rt = reinterpret_cast<const float2 *>(a.rope);
+  const int col = lane & 15, kg = lane >> 4;
   for (int u = u0; u < u1; ++u) {
-    const int b = u / (nkv * NC), g = (u / NC) % nkv, c = u % NC;
-    const int seq = a.verify ? 0 : b;
+    const int row = u / (nkv * NC), g = (u / NC) % nkv, c = u % NC;
+    const int seq = a.verify ? 0 : row;
     const int pbase = pos_of(a, seq);
-    const int maxpos = pbase + nrow - 1;
-    const int c0 = c * CS;
-    const int c1 = min(c0 + CS, min(a.max_ctx, maxpos + 1));  // positions [c0, c1) are read
-    const int npos = max(c1 - c0, 0);
-    lds_barrier();
-    if (tid < nrow) rpos[tid] = pbase + tid;
-    // queries (sum of k-split partials)
-    for (int idx = tid; idx < Q * HD; idx += kThreads) {
-      const int qi = idx / HD, i = idx % HD, rr = qi / grp, hh = qi % grp;
-      const int row = a.verify ? rr : b;
-      const int h = g * grp + hh;
-      float s = 0.0f;
-      for (int s2 = 0; s2 < ph.src_S; ++s2) s += src[((size_t)s2 * R + row) * ph.src_N + ph.q_off + h * HD + i];
-      qs[qi * HD + i] = s;
-    }
-    // cached K/V rows of the chunk
-    for (int idx = tid; idx < npos * (HD / 8); idx += kThreads) {
-      const int jj = idx / (HD / 8), i8 = (idx % (HD / 8)) * 8, j = c0 + jj;
-      if (j < pbase) {
-        const size_t off = (((size_t)seq * nkv + g) * a.max_ctx + j) * HD + i8;
-        *reinterpret_cast<uint4 *>(Ks + jj * HD + i8) = *reinterpret_cast<const uint4 *>(kc + off);
-        *reinterpret_cast<uint4 *>(Vs + jj * HD + i8) = *reinterpret_cast<const uint4 *>(vc + off);
-      }
-    }
-    // this step's new rows: rotated K and V rounded to bf16, appended to the cache
-    for (int idx = tid; idx < npos * half; idx += kThreads) {
-      const int jj = idx / half, i = idx % half, j = c0 + jj;
-      if (j >= pbase) {
-        const int row = a.verify ? (j - pbase) : b;
-        float k0 = 0, k1 = 0, v0 = 0, v1 = 0;
-        for (int s2 = 0; s2 < ph.src_S; ++s2) {
-          const float *pr = src + ((size_t)s2 * R + row) * ph.src_N;
-          k0 += pr[ph.k_off + g * HD + i];
-          k1 += pr[ph.k_off + g * HD + i + half];
-          v0 += pr[ph.v_off + g * HD + i];
-          v1 += pr[ph.v_off + g * HD + i + half];
-        }
-        const float2 cs = reinterpret_cast<const float2 *>(a.rope)[(size_t)j * half + i];
-        const uint16_t kr0 = f2bf(k0 * cs.x - k1 * cs.y), kr1 = f2bf(k0 * cs.y + k1 * cs.x);
-        const uint16_t vb0 = f2bf(v0), vb1 = f2bf(v1);
-        Ks[jj * HD + i] = kr0;
-        Ks[jj * HD + i + half] = kr1;
-        Vs[jj * HD + i] = vb0;
-        Vs[jj * HD + i + half] = vb1;
-        const size_t off = (((size_t)seq * nkv + g) * a.max_ctx + j) * HD;
-        kc[off + i] = kr0;
-        kc[off + i + half] = kr1;
-        vc[off + i] = vb0;
-        vc[off + i + half] = vb1;
-      }
-    }
-    lds_barrier();
-    for (int idx = tid; idx < Q * half; idx += kThreads) {  // rotate the queries
-      const int qi = idx / half, i = idx % half, rr = qi / grp;
-      const float2 cs = reinterpret_cast<const float2 *>(a.rope)[(size_t)rpos[rr] * half + i];
-      const float x0 = qs[qi * HD + i], x1 = qs[qi * HD + i + half];
-      qs[qi * HD + i] = x0 * cs.x - x1 * cs.y;
-      qs[qi * HD + i + half] = x0 * cs.y + x1 * cs.x;
-    }
-    lds_barrier();
-    // scores: one thread per (query, position), the HD-long dot product fully unrolled
-    for (int idx = tid; idx < Q * CS; idx += kThreads) {
-      const int qi = idx / CS, jj = idx % CS, j = c0 + jj;
-      float s = -INFINITY;
-      if (jj < npos && j <= rpos[qi / grp]) {
-        const float4 *qv = reinterpret_cast<const float4 *>(qs + qi * HD);
-        const uint4 *kv = reinterpret_cast<const uint4 *>(Ks + jj * HD);
-        float acc = 0.0f;
+    const int prow = pbase + (a.verify ? row : 0);
+    const int j0 = c * CS, j1 = min(j0 + CS, prow + 1);
+    const size_t cbase = ((size_t)seq * nkv + g) * a.max_ctx;
+    lds_barrier();  // the previous unit's LDS reads are done
+    // queries of the group (rotated at prow) as the B operand
+    for (int it = tid; it < 8 * (HD / 8); it += kThreads) {
+      const int hl = it / (HD / 8), d0 = (it - hl * (HD / 8)) * 8;
+      float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (hl < grp) {
+        const int h = g * grp + hl, pr = d0 < half ? d0 + half : d0 - half;
 #pragma unroll
-        for (int i = 0; i < HD / 8; ++i) {
-          const uint4 kk = kv[i];
-          const float4 qa = qv[2 * i], qb = qv[2 * i + 1];
-          acc += qa.x * bf2f((uint16_t)kk.x) + qa.y * bf2f((uint16_t)(kk.x >> 16)) + qa.z * bf2f((uint16_t)kk.y) +
-                 qa.w * bf2f((uint16_t)(kk.y >> 16)) + qb.x * bf2f((uint16_t)kk.z) + qb.y * bf2f((uint16_t)(kk.z >> 16)) +
-                 qb.z * bf2f((uint16_t)kk.w) + qb.w * bf2f((uint16_t)(kk.w >> 16));
+        for (int e = 0; e < 8; ++e) {
+          float x = 0.0f, xp = 0.0f;
+          for (int s2 = 0; s2 < ph.src_S; ++s2) {
+            const float *qr = src + ((size_t)s2 * R + row) * ph.src_N + ph.q_off + h * HD;
+            x += qr[d0 + e];
+            xp += qr[pr + e];
+          }
+          const float2 cs = rt[(size_t)prow * half + (d0 + e) % half];
+          y[e] = d0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
         }
-        s = acc * scale;
       }
-      sc[qi * CS + jj] = s;
+      const int ks = d0 >> 5, kk = (d0 >> 3) & 3;
+      Qb[(ks * 4 + kk) * 16 + hl] = pack_hi_lo(y, false);
+      Qb[(ks * 4 + kk) * 16 + hl + 8] = pack_hi_lo(y, true);
     }
-    lds_barrier();
-    // softmax statistics: one wave per query, lanes over positions
-    for (int qi = wave; qi < Q; qi += kWavesTotal) {
-      float m = -INFINITY;
-      for (int jj = lane; jj < CS; jj += 64) m = fmaxf(m, sc[qi * CS + jj]);
+    if (tid < 8) { mst[tid] = -INFINITY; lst[tid] = 0.0f; }
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int jb = j0; jb < j1; jb += kGqaSub) {
+      lds_barrier();
+      // K/V rows of the block; this step's rows from the projections (rotated K, bf16), appended once
+      for (int it = tid; it < kGqaSub * (HD / 8); it += kThreads) {
+        const int jj = it / (HD / 8), d0 = (it - jj * (HD / 8)) * 8, j = jb + jj;
+        uint4 kv = uint4{0u, 0u, 0u, 0u}, vv = uint4{0u, 0u, 0u, 0u};
+        if (j < j1) {
+          if (j < pbase) {
+            kv = *reinterpret_cast<const uint4 *>(kc + (cbase + j) * HD + d0);
+            vv = *reinterpret_cast<const uint4 *>(vc + (cbase + j) * HD + d0);
+          } else {
+            const int rr = a.verify ? j - pbase : row;
+            const int pr = d0 < half ? d0 + half : d0 - half;
+            float yk[8], yv[8];
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      float l = 0.0f;
-      for (int jj = lane; jj < CS; jj += 64) {
-        const float p = (m == -INFINITY) ? 0.0f : __expf(sc[qi * CS + jj] - m);
-        sc[qi * CS + jj] = p;
-        l += p;
+            for (int e = 0; e < 8; ++e) {
+              float x = 0.0f, xp = 0.0f, v = 0.0f;
+              for (int s2 = 0; s2 < ph.src_S; ++s2) {
+                const float *pp = src + ((size_t)s2 * R + rr) * ph.src_N;
+                x += pp[ph.k_off + g * HD + d0 + e];
+                xp += pp[ph.k_off + g * HD + pr + e];
+                v += pp[ph.v_off + g * HD + d0 + e];
+              }
+              const float2 cs = rt[(size_t)j * half + (d0 + e) % half];
+              yk[e] = d0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
+              yv[e] = v;
+            }
+            kv = pack_hi_lo(yk, false);
+            vv = pack_hi_lo(yv, false);
+            if (a.verify ? row == R - 1 : true) {  // one unit appends each new row
+              *reinterpret_cast<uint4 *>(kc + (cbase + j) * HD + d0) = kv;
+              *reinterpret_cast<uint4 *>(vc + (cbase + j) * HD + d0) = vv;
+            }
+          }
+        }
+        *reinterpret_cast<uint4 *>(Ks + jj * L::rowb + d0 * 2) = kv;
+        *reinterpret_cast<uint4 *>(Vs + jj * L::rowb + d0 * 2) = vv;
       }
-      l = wave_sum(l);
-      if (lane == 0) { ml[qi * 2] = m; ml[qi * 2 + 1] = l; }
+      lds_barrier();
+      if (wave < kCWaves) {  // scores: wave w takes positions jb + 16 w .. +15
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 av = *reinterpret_cast<const uint4 *>(Ks + (wave * 16 + col) * L::rowb + (ks * 32 + kg * 8) * 2);
+          const uint4 bv = Qb[(ks * 4 + kg) * 16 + col];
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), sacc, 0,
+                                                         0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = sacc[e] + __shfl_down(sacc[e], 8);
+          const int pl = wave * 16 + kg * 4 + e;
+          if (col < 8) Sc[pl * 8 + col] = (jb + pl < j1) ? v * scale : -INFINITY;
+        }
+      }
+      lds_barrier();
+      if (tid < 8 * 16) {  // online softmax: 16 lanes per query, 4 positions each
+        const int h = tid >> 4, q = tid & 15;
+        float sv[4], bm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = Sc[(q * 4 + e) * 8 + h];
+          bm = fmaxf(bm, sv[e]);
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o));
+        const float mo = mst[h], mn = fmaxf(mo, bm);
+        float pv[4], ls = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = mn == -INFINITY ? 0.0f : __expf(sv[e] - mn);
+          ls += pv[e];
+        }
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
+        const float o4[4] = {__shfl_xor(pv[0], 1), __shfl_xor(pv[1], 1), __shfl_xor(pv[2], 1), __shfl_xor(pv[3], 1)};
+        if ((q & 1) == 0) {
+          const float y[8] = {pv[0], pv[1], pv[2], pv[3], o4[0], o4[1], o4[2], o4[3]};
+          const int gg = q >> 1, kp = gg >> 2, kk = gg & 3;
+          Pb[(kp * 4 + kk) * 16 + h] = pack_hi_lo(y, false);
+          Pb[(kp * 4 + kk) * 16 + h + 8] = pack_hi_lo(y, true);
+        }
+        if (q == 0) {
+          const float al = mo == -INFINITY ? 0.0f : __expf(mo - mn);
+          alp[h] = al;
+          mst[h] = mn;
+          lst[h] = lst[h] * al + ls;
+        }
+      }
+      lds_barrier();
+      if (wave < kCWaves) {  // out^T += V^T P: wave w takes dims w * HD/4 .. (HD/64 row blocks)
+        const float al = alp[col & 7];
+#pragma unroll
+        for (int rb = 0; rb < HD / 64; ++rb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rb][e] *= al;
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const uint4 bv = Pb[(kp * 4 + kg) * 16 + col];
+#pragma unroll
+          for (int rb = 0; rb < HD / 64; ++rb) {
+            const int dim = wave * (HD / 4) + rb * 16 + col;
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+              const uint16_t lo16 = *reinterpret_cast<const uint16_t *>(Vs + (kp * 32 + kg * 8 + i) * L::rowb + dim * 2);
+              const uint16_t hi16 = *reinterpret_cast<const uint16_t *>(Vs + (kp * 32 + kg * 8 + i + 1) * L::rowb + dim * 2);
+              w[i >> 1] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
+            }
+            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, uint4{w[0], w[1], w[2], w[3]}),
+                                                              __builtin_bit_cast(bf16x8, bv), acc[rb], 0, 0, 0);
+          }
+        }
+      }
     }
-    lds_barrier();
-    // weighted values: one thread per (query, output dim)
-    for (int idx = tid; idx < Q * HD; idx += kThreads) {
-      const int qi = idx / HD, i = idx % HD, rr = qi / grp, hh = qi % grp;
-      float acc = 0.0f;
-      const float *pr = sc + qi * CS;
-#pragma unroll 8
-      for (int jj = 0; jj < npos; ++jj) acc += pr[jj] * bf2f(Vs[jj * HD + i]);
-      const int row = a.verify ? rr : b, h = g * grp + hh;
-      float *dst = a.attn + (((size_t)row * nq + h) * NC + c) * (HD + 2);
-      st_c(dst + 2 + i, acc);
-      if (i == 0) { st_c(dst, ml[qi * 2]); st_c(dst + 1, ml[qi * 2 + 1]); }
+    lds_barrier();  // final statistics visible
+    const int W = HD + 2;
+    if (wave < kCWaves) {
+#pragma unroll
+      for (int rb = 0; rb < HD / 64; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[rb][e] + __shfl_down(acc[rb][e], 8);
+          if (col < grp && col < 8) {
+            const int dim = wave * (HD / 4) + rb * 16 + kg * 4 + e;
+            st_c(a.attn + (((size_t)row * nq + g * grp + col) * NC + c) * W + 2 + dim, v);
+          }
+        }
+    }
+    if (tid < grp) {
+      float *dst = a.attn + (((size_t)row * nq + g * grp + tid) * NC + c) * W;
+      st_c(dst, mst[tid]);
+      st_c(dst + 1, lst[tid]);
     }
   }
 }
@@ -1129,16 +1209,6 @@ struct MlaLds {
 };
 static_assert(MlaLds::end <= kLdsBytes, "latent attention LDS layout exceeds the workgroup's LDS");
 
-__device__ __forceinline__ uint4 pack_hi_lo(const float (&y)[8], bool lo) {
-  uint32_t w[4];
-#pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    uint16_t h0 = f2bf(y[e]), h1 = f2bf(y[e + 1]);
-    if (lo) { h0 = f2bf(y[e] - bf2f(h0)); h1 = f2bf(y[e + 1] - bf2f(h1)); }
-    w[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-  }
-  return uint4{w[0], w[1], w[2], w[3]};
-}
 
 __device__ __forceinline__ void mla_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, tid = threadIdx.x, lane = tid & 63;

@@ -161,8 +161,8 @@ mk_status validate(const mk_config *c) {
       return fail(MK_E_ARG, "n_q_heads %d must be a positive multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
     if (c->head_dim != 64 && c->head_dim != 128) return fail(MK_E_UNSUPPORTED, "head_dim %d (64 or 128 supported)", c->head_dim);
     if ((c->n_q_heads * c->head_dim) % 256) return fail(MK_E_UNSUPPORTED, "n_q_heads * head_dim must be a multiple of 256");
-    if ((c->n_q_heads / c->n_kv_heads) * kMaxRows > kAttnMaxQ)
-      return fail(MK_E_UNSUPPORTED, "query heads per kv head %d exceed %d", c->n_q_heads / c->n_kv_heads, kAttnMaxQ / kMaxRows);
+    if (c->n_q_heads / c->n_kv_heads > 8)
+      return fail(MK_E_UNSUPPORTED, "query heads per kv head %d exceed 8", c->n_q_heads / c->n_kv_heads);
     if (!(c->rope_theta > 0.0f)) return fail(MK_E_ARG, "rope_theta must be positive");
   }
   if (any_mla) {
@@ -253,10 +253,10 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
   if (f.n_q_heads > 0) {
     const int nseq_max = R;  // decode: R sequences; verify (R = 8): 1 sequence, 8 query rows
     double best = 1e300;
-    for (int cs = 16; cs <= kAttnMaxChunk; cs += 16) {
+    for (int cs = 64; cs <= 64 * ((f.max_ctx + 63) / 64); cs += 64) {
       const int nc = (f.max_ctx + cs - 1) / cs;
       const int64_t units = (int64_t)nseq_max * f.n_kv_heads * nc;
-      const double cost = (double)((units + G - 1) / G) * (cs + 48);
+      const double cost = (double)((units + G - 1) / G) * (cs + 64) + 1e-3 * nc;
       if ((int64_t)nc * (f.head_dim + 2) * 4 + (nc + 1) * 4 > kLdsBytes) continue;  // merge stages all chunks in LDS
       if (cost < best) { best = cost; sc.chunk = cs; sc.n_chunks = nc; }
     }

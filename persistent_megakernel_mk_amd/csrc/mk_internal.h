@@ -11,15 +11,13 @@ constexpr int kWavesTotal = kCWaves + 1;
 constexpr int kThreads = kWavesTotal * 64;  // threads per workgroup
 constexpr int kCThreads = kCWaves * 64;     // threads of the compute waves
 constexpr int kRing = 12;                 // weight items in flight per compute wave (12 KiB), bf16 build
-constexpr int kRingNvfp4 = 12;            // the same for the build that also streams NVFP4 items
+constexpr int kRingNvfp4 = 10;            // the same for the build that also streams NVFP4 items
 constexpr int kTileRows = 16;             // weight rows per MFMA tile
 constexpr int kFragK = 32;                // reduction columns per 1 KiB weight fragment
 constexpr int kLdsBytes = 160 * 1024 - 512;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU, minus static)
 constexpr int kActLdsBudget = 96 * 1024;  // activation fragments of one k-split
 constexpr int kMaxRows = 8;               // rows per step (batch or verify block)
-constexpr int kAttnMaxChunk = 128;        // positions per split-KV chunk
 constexpr int kMaxUnits = 512;            // product units (tile x k-split) per workgroup and phase
-constexpr int kAttnMaxQ = 64;             // queries per split-KV unit (query heads per kv head x rows)
 constexpr int kMaxTopK = 16;              // routed experts per token
 constexpr int kMaxExperts = 1024;         // routed experts per MoE layer
 constexpr int kMaxShared = 4;             // shared experts per MoE layer
