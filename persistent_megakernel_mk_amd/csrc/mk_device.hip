@@ -776,6 +776,7 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   const float *ts = reinterpret_cast<const float *>(a.wbuf + ph.ts_off);
   const int nrot = u1 - u0, r0 = rotated(ph) ? rot_start(s, ph.S, nrot) : 0;
   const bool fin = needs_finalise(ph);
+  const bool direct_resid = ph.out == OUT_RESID && S_eff == 1;
   for (int unit = 0; unit < nrot; ++unit) {
     const int u = u0 + (r0 + unit < nrot ? r0 + unit : r0 + unit - nrot);
     const int sl = unit % kRedSlots;
@@ -793,6 +794,7 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     if (lds_ld(posted + sl) < need) lds_wait_ge(posted + sl, need, a);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     const float *rb = red + sl * kCWaves * 16 * kMaxRows;
+    float xsq[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int idx = lane + 64 * k;
@@ -806,6 +808,11 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
           const int n = u * kTileRows + row;
           a.logits[(size_t)b * a.V + n] = v;
           if (v > best_v[k]) { best_v[k] = v; best_i[k] = n; }
+        } else if (direct_resid) {  // one contributor: the unit's values are final
+          const int n = u * kTileRows + row;
+          const float xn = ld_c(a.x + (size_t)b * a.H + n) + v;
+          st_c(a.x + (size_t)b * a.H + n, xn);
+          xsq[k] = xn * xn;
         } else if (expert && ph.out == OUT_RESID) {
           st_c(part_of(a, ph.dst_part) + ((size_t)(j * ph.S + s) * R + b) * TN + tl * kTileRows + row, v);
         } else {
@@ -815,7 +822,19 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_store(consumed + sl, (uint32_t)(unit / kRedSlots + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (fin) {
+    if (direct_resid) {  // the tile's sum of squares per row: lanes hold (row = idx / R, b = idx % R)
+      float *sqs = misc + 16 + kMaxUnits + 256;  // [16][kMaxRows]
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (lane + 64 * k < 16 * R) sqs[lane + 64 * k] = xsq[k];
+      wave_lds_sync();
+      if (lane < R) {
+        float v = 0.0f;
+        for (int row = 0; row < 16; ++row) v += sqs[row * R + lane];
+        st_c(a.ss + (size_t)lane * (a.H / kTileRows) + u, v);
+      }
+      wave_lds_sync();
+    } else if (fin) {
       // count this contribution as soon as its partials are acknowledged; the last contributor of the
       // tile finalises it right away (while the compute waves stream the remaining units) and resets
       // the tile's counter for the next step

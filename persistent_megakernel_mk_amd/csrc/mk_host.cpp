@@ -191,7 +191,7 @@ mk_status validate(const mk_config *c) {
 // time per unit for the cross-wave reduction). A product of nseg segments of segT tiles each gives every
 // segment its own activation when per_seg_act (one piece per segment a workgroup's units touch).
 int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_seg_act = false, bool fp4 = false,
-                  int *pieces_out = nullptr) {
+                  int *pieces_out = nullptr, bool resid = false) {
   int best = -1, best_pieces = 1;
   double best_cost = 1e300;
   const int64_t U = (int64_t)segT * nseg;
@@ -205,7 +205,11 @@ int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_
     const int np = per_seg_act ? (int)std::min<int64_t>((per - 1 + segT - 1) / segT + 1, nseg) : 1;
     if (np > kMaxPieces) continue;
     if ((int64_t)np * nf * 128 * R > kActLdsBudget) continue;
-    const double cost = (double)per * (nf / kCWaves + 1.0) + 0.01 * S;
+    // a residual product split over k also pays, per unit, the acknowledgement of its partials and the
+    // tile counter round trip (about ten fragment times); with one split the unit adds into the
+    // residual directly
+    const double fin = (resid && S > 1) ? 10.0 * per : 0.0;
+    const double cost = (double)per * (nf / kCWaves + 1.0) + fin + 0.01 * S;
     if (cost < best_cost) { best_cost = cost; best = S; best_pieces = np; }
   }
   if (pieces_out) *pieces_out = best_pieces;
@@ -213,6 +217,7 @@ int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_
 }
 
 Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S) {
+  const bool resid = out == OUT_RESID;
   Phase p;
   memset(&p, 0, sizeof(p));
   p.type = PH_GEMV;
@@ -221,7 +226,7 @@ Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S) {
   p.K = w.K;
   p.T = w.N / kTileRows;
   p.KF = w.K / kFragK;
-  p.S = choose_splits(p.T, 1, p.KF, R, G, max_S);
+  p.S = choose_splits(p.T, 1, p.KF, R, G, max_S, false, false, nullptr, resid);
   p.nf = p.S > 0 ? p.KF / p.S : 0;
   p.act = act;
   p.out = out;
