@@ -51,6 +51,22 @@ __device__ __forceinline__ int32_t ld_ci(const int32_t *p) {
 __device__ __forceinline__ void st_ci(int32_t *p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Device-coherent loads of 2 and 4 floats (8-byte atomic loads): read other workgroups' results of
+// earlier phases without invalidating this XCD's caches at every grid barrier.
+__device__ __forceinline__ float2 ld_c2(const float *p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ float4 ld_c4(const float *p) {
+  const float2 lo = ld_c2(p), hi = ld_c2(p + 2);
+  return make_float4(lo.x, lo.y, hi.x, hi.y);
+}
+// acc[e] += p[e], e < 8, from another workgroup's results (device-coherent; p 8-byte aligned)
+__device__ __forceinline__ void add8(float (&acc)[8], const float *p) {
+  const float4 lo = ld_c4(p), hi = ld_c4(p + 4);
+  acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+  acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+}
 __device__ __forceinline__ uint32_t ld_cu(const uint32_t *p) {
   return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -104,9 +120,13 @@ __device__ bool grid_arrive_wait(CArgs &a, uint32_t k, int phase) {
   const uint32_t tgt = k * groups;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   bool ok = true;
-  while ((int32_t)(ld_cu(a.bar + 8 * 32) - tgt) < 0) {
-    __builtin_amdgcn_s_sleep(2);
-    if (ld_ci(a.status + 2) != 0) { ok = false; break; }
+  for (uint32_t it = 0;; ++it) {
+    // the barrier word and (every 16th poll) the abort flag are loaded together
+    const uint32_t v = ld_cu(a.bar + 8 * 32);
+    const int32_t ab = (it & 15u) == 15u ? ld_ci(a.status + 2) : 0;
+    if ((int32_t)(v - tgt) >= 0) break;
+    if (ab != 0) { ok = false; break; }
+    __builtin_amdgcn_s_sleep(1);
     if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > a.timeout_ticks) {
       st_ci(a.status + 1, phase);
       st_ci(a.status + 0, 6 /* MK_E_DEVICE_TIMEOUT */);
@@ -115,7 +135,9 @@ __device__ bool grid_arrive_wait(CArgs &a, uint32_t k, int phase) {
       break;
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // drop stale L1/L2 lines before the next phase reads
+  // every later read of another workgroup's result is a device-coherent load, so no cache is
+  // invalidated here; the fence keeps the compiler from moving those loads above the wait
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return ok;
 }
 
@@ -465,8 +487,8 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
     const int off = ph.src_off + j * ph.src_seg + k;
     float y[8];
     if (ph.act == ACT_NORM) {
-      const float4 *xp = reinterpret_cast<const float4 *>(a.x + (size_t)b * a.H + k);
-      float4 x0 = xp[0], x1 = xp[1];
+      const float *xp = a.x + (size_t)b * a.H + k;
+      const float4 x0 = ld_c4(xp), x1 = ld_c4(xp + 4);
       const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.wbuf + ph.gain_off) + k;
       uint4 gg = *reinterpret_cast<const uint4 *>(gp);
       float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -477,19 +499,19 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
         y[e] = xs[e] * g;
       }
     } else if (ph.act == ACT_MIX) {
-      const float4 *mp = reinterpret_cast<const float4 *>(a.mix + (size_t)b * a.mix_stride + off);
-      float4 m0 = mp[0], m1 = mp[1];
+      const float *mp = a.mix + (size_t)b * a.mix_stride + off;
+      const float4 m0 = ld_c4(mp), m1 = ld_c4(mp + 4);
       y[0] = m0.x; y[1] = m0.y; y[2] = m0.z; y[3] = m0.w; y[4] = m1.x; y[5] = m1.y; y[6] = m1.z; y[7] = m1.w;
     } else {
       const float *src = part_of(a, ph.src_part);
       float g[8] = {0, 0, 0, 0, 0, 0, 0, 0}, u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int s2 = 0; s2 < ph.src_S; ++s2) {
         const float *row = src + ((size_t)s2 * R + b) * ph.src_N + off;
-        float4 p0 = reinterpret_cast<const float4 *>(row)[0], p1 = reinterpret_cast<const float4 *>(row)[1];
+        const float4 p0 = ld_c4(row), p1 = ld_c4(row + 4);
         g[0] += p0.x; g[1] += p0.y; g[2] += p0.z; g[3] += p0.w; g[4] += p1.x; g[5] += p1.y; g[6] += p1.z; g[7] += p1.w;
         if (ph.act == ACT_SWIGLU) {
           const float *up = row + ph.K;  // up rows follow the gate rows
-          float4 q0 = reinterpret_cast<const float4 *>(up)[0], q1 = reinterpret_cast<const float4 *>(up)[1];
+          const float4 q0 = ld_c4(up), q1 = ld_c4(up + 4);
           u[0] += q0.x; u[1] += q0.y; u[2] += q0.z; u[3] += q0.w; u[4] += q1.x; u[5] += q1.y; u[6] += q1.z; u[7] += q1.w;
         }
       }
@@ -761,7 +783,7 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     const int nt = a.H / kTileRows;
     for (int b = 0; b < R; ++b) {
       float v = 0.0f;
-      for (int t = lane; t < nt; t += 64) v += a.ss[(size_t)b * nt + t];
+      for (int t = lane; t < nt; t += 64) v += ld_c(a.ss + (size_t)b * nt + t);
       v = wave_sum(v);
       if (lane == 0) rstd[b] = 1.0f / sqrtf(v / (float)a.H + a.eps);
     }
@@ -919,7 +941,7 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
         const int off = (kind == 0 ? ph.q_off : ph.k_off) + h * dk + c0;
         float x0 = 0.0f, x1 = 0.0f;
         for (int s2 = 0; s2 < ph.src_S; ++s2) {
-          const float2 p2 = *reinterpret_cast<const float2 *>(src + ((size_t)s2 * R + row) * ph.src_N + off);
+          const float2 p2 = ld_c2(src + ((size_t)s2 * R + row) * ph.src_N + off);
           x0 += p2.x;
           x1 += p2.y;
         }
@@ -932,14 +954,14 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
         for (int s2 = 0; s2 < ph.src_S; ++s2) {
           const float *pr = src + ((size_t)s2 * R + row) * ph.src_N;
           if (ph.per_channel_gate) {
-            const float2 p2 = *reinterpret_cast<const float2 *>(pr + ph.a_off + h * dk + c0);
+            const float2 p2 = ld_c2(pr + ph.a_off + h * dk + c0);
             a0 += p2.x;
             a1 += p2.y;
           } else {
-            a0 += pr[ph.a_off + h];
+            a0 += ld_c(pr + ph.a_off + h);
           }
-          bb += pr[ph.b_off + h];
-          if (lane < RPU) vr += pr[ph.v_off + h * dv + rb * RPU + lane];
+          bb += ld_c(pr + ph.b_off + h);
+          if (lane < RPU) vr += ld_c(pr + ph.v_off + h * dv + rb * RPU + lane);
         }
         if (!ph.per_channel_gate) a1 = a0;
         al[j * 128 + c0] = __expf(-softplusf_(a0));
@@ -1048,16 +1070,16 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
       float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (hl < grp) {
         const int h = g * grp + hl, pr = d0 < half ? d0 + half : d0 - half;
+        float x[8] = {0, 0, 0, 0, 0, 0, 0, 0}, xp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int s2 = 0; s2 < ph.src_S; ++s2) {
+          const float *qr = src + ((size_t)s2 * R + row) * ph.src_N + ph.q_off + h * HD;
+          add8(x, qr + d0);
+          add8(xp, qr + pr);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float x = 0.0f, xp = 0.0f;
-          for (int s2 = 0; s2 < ph.src_S; ++s2) {
-            const float *qr = src + ((size_t)s2 * R + row) * ph.src_N + ph.q_off + h * HD;
-            x += qr[d0 + e];
-            xp += qr[pr + e];
-          }
           const float2 cs = rt[(size_t)prow * half + (d0 + e) % half];
-          y[e] = d0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
+          y[e] = d0 < half ? x[e] * cs.x - xp[e] * cs.y : xp[e] * cs.y + x[e] * cs.x;
         }
       }
       const int ks = d0 >> 5, kk = (d0 >> 3) & 3;
@@ -1079,19 +1101,17 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
           } else {
             const int rr = a.verify ? j - pbase : row;
             const int pr = d0 < half ? d0 + half : d0 - half;
-            float yk[8], yv[8];
+            float yk[8], x[8] = {0, 0, 0, 0, 0, 0, 0, 0}, xp[8] = {0, 0, 0, 0, 0, 0, 0, 0}, yv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            for (int s2 = 0; s2 < ph.src_S; ++s2) {
+              const float *pp = src + ((size_t)s2 * R + rr) * ph.src_N;
+              add8(x, pp + ph.k_off + g * HD + d0);
+              add8(xp, pp + ph.k_off + g * HD + pr);
+              add8(yv, pp + ph.v_off + g * HD + d0);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              float x = 0.0f, xp = 0.0f, v = 0.0f;
-              for (int s2 = 0; s2 < ph.src_S; ++s2) {
-                const float *pp = src + ((size_t)s2 * R + rr) * ph.src_N;
-                x += pp[ph.k_off + g * HD + d0 + e];
-                xp += pp[ph.k_off + g * HD + pr + e];
-                v += pp[ph.v_off + g * HD + d0 + e];
-              }
               const float2 cs = rt[(size_t)j * half + (d0 + e) % half];
-              yk[e] = d0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
-              yv[e] = v;
+              yk[e] = d0 < half ? x[e] * cs.x - xp[e] * cs.y : xp[e] * cs.y + x[e] * cs.x;
             }
             kv = pack_hi_lo(yk, false);
             vv = pack_hi_lo(yv, false);
@@ -1270,17 +1290,16 @@ __device__ __forceinline__ void mla_phase(CArgs &a, const Phase &ph, char *smem)
         } else {
           const int r0 = d0 - rank;  // rotary dims r0..r0+7, partner dims at +-half
           const int pr = r0 < half ? r0 + half : r0 - half;
+          float x[8] = {0, 0, 0, 0, 0, 0, 0, 0}, xp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+          for (int s2 = 0; s2 < ph.src_S; ++s2) {
+            const float *pr_row = src + ((size_t)s2 * R + row) * ph.src_N + ph.q_off + h * ph.qk_stride + ph.nope;
+            add8(x, pr_row + r0);
+            add8(xp, pr_row + pr);
+          }
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float x = 0.0f, xp = 0.0f;
-            for (int s2 = 0; s2 < ph.src_S; ++s2) {
-              const float *pr_row = src + ((size_t)s2 * R + row) * ph.src_N + ph.q_off + h * ph.qk_stride + ph.nope;
-              x += pr_row[r0 + e];
-              xp += pr_row[pr + e];
-            }
-            const int i = (r0 + e) % half;
-            const float2 cs = rt[(size_t)prow * half + i];
-            y[e] = r0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
+            const float2 cs = rt[(size_t)prow * half + (r0 + e) % half];
+            y[e] = r0 < half ? x[e] * cs.x - xp[e] * cs.y : xp[e] * cs.y + x[e] * cs.x;
           }
         }
       }
@@ -1306,24 +1325,20 @@ __device__ __forceinline__ void mla_phase(CArgs &a, const Phase &ph, char *smem)
             float y[8];
             if (d0 < rank) {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                float x = 0.0f;
-                for (int s2 = 0; s2 < ph.src_S; ++s2) x += src[((size_t)s2 * R + rr) * ph.src_N + ph.dkv_off + d0 + e];
-                y[e] = x;
-              }
+              for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+              for (int s2 = 0; s2 < ph.src_S; ++s2) add8(y, src + ((size_t)s2 * R + rr) * ph.src_N + ph.dkv_off + d0);
             } else {
               const int r0 = d0 - rank, pr = r0 < half ? r0 + half : r0 - half;
+              float x[8] = {0, 0, 0, 0, 0, 0, 0, 0}, xp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+              for (int s2 = 0; s2 < ph.src_S; ++s2) {
+                const float *kr = src + ((size_t)s2 * R + rr) * ph.src_N + ph.kr_off;
+                add8(x, kr + r0);
+                add8(xp, kr + pr);
+              }
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
-                float x = 0.0f, xp = 0.0f;
-                for (int s2 = 0; s2 < ph.src_S; ++s2) {
-                  const float *kr = src + ((size_t)s2 * R + rr) * ph.src_N + ph.kr_off;
-                  x += kr[r0 + e];
-                  xp += kr[pr + e];
-                }
-                const int i = (r0 + e) % half;
-                const float2 cs = rt[(size_t)j * half + i];
-                y[e] = r0 < half ? x * cs.x - xp * cs.y : xp * cs.y + x * cs.x;
+                const float2 cs = rt[(size_t)j * half + (r0 + e) % half];
+                y[e] = r0 < half ? x[e] * cs.x - xp[e] * cs.y : xp[e] * cs.y + x[e] * cs.x;
               }
             }
             v = pack_hi_lo(y, false);
@@ -1451,7 +1466,7 @@ __device__ __forceinline__ void merge_phase(CArgs &a, const Phase &ph, char *sme
     const int row = u / nq, h = u % nq;
     const float *p = a.attn + ((size_t)row * nq + h) * NC * W;
     lds_barrier();
-    for (int i = tid; i < NC * W; i += kThreads) pl[i] = p[i];
+    for (int i = tid; i < NC * W; i += kThreads) pl[i] = ld_c(p + i);
     lds_barrier();
     if (tid < 64) {  // one wave: global max and normaliser over chunks, in chunk order per lane
       float M = -INFINITY;
@@ -1521,8 +1536,8 @@ __device__ __forceinline__ void final_phase(CArgs &a, char *smem) {
   int *acc_s = am + kMaxRows;
   if (a.V > 0) {
     for (int idx = tid; idx < G * R; idx += kThreads) {
-      cv[idx] = a.cand[(size_t)idx * 2];
-      ci[idx] = reinterpret_cast<const int32_t *>(a.cand)[(size_t)idx * 2 + 1];
+      cv[idx] = ld_c(a.cand + (size_t)idx * 2);
+      ci[idx] = ld_ci(reinterpret_cast<const int32_t *>(a.cand) + (size_t)idx * 2 + 1);
     }
     lds_barrier();
     if (tid < R) {
