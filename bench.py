@@ -8,7 +8,12 @@ megakernel: embedding, all 64 layers, final norm, LM head and argmax. Timed with
 stream the kernel runs on. Also reported: batch 8, the per-op (one launch per phase) baseline, and the
 CPU oracle on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+Other workloads (--config): c2, the same stack's 8-row verify step (anchor + 7 drafts); c3, a Kimi-class
+slice (3 Kimi-delta-attention : 1 absorbed latent attention layer, 384 bf16 experts top-8 + 1 shared,
+hidden 7168) at batch 8; c4, an NVFP4-expert slice (8 GQA layers, 256 experts top-8 + 1 shared, hidden
+6144) at batch 1 and 8. Mixture-of-experts steps count the experts of the batch's actual union.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c1|c2|c3|c4] [--batches 1,8]
 """
 from __future__ import annotations
 
@@ -29,54 +34,105 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_gpu(cfg, max_batch):
+def build_gpu(cfg, max_batch, expert_pool=8):
+    """Generates the configuration's weights and states in device memory and packs them. bf16 tensors come
+    from the device generator. NVFP4 expert matrices are encoded on the host (seeded normals quantised
+    onto the E2M1 x E4M3 grid); to keep that bounded, each projection kind uses a pool of `expert_pool`
+    distinct encoded matrices, assigned to the experts in turn. Every expert still has its own packed
+    copy, so the bytes a step streams are those of distinct experts; only the values repeat."""
+    import re
+
     import torch
 
     from persistent_megakernel_mk_amd import mk, synth
 
     m = mk.Megakernel(cfg, device=0, max_batch=max_batch)
     t0 = time.time()
-    descs = []
+    pool = {}
+    n_fp4 = 0
     for spec in synth.weight_specs(cfg):
-        t = synth.generate_gpu(spec, cfg.seed)
         layer, kind, expert = mk.weight_target(spec.name)
         d = mk.WeightDesc()
-        d.layer, d.kind, d.expert, d.dtype = layer, kind, expert, 0
-        d.rows, d.cols = (1, spec.shape[0]) if len(spec.shape) == 1 else spec.shape
-        d.data = t.data_ptr()
+        d.layer, d.kind, d.expert = layer, kind, expert
+        if spec.kind == "nvfp4":
+            proj = spec.name.rsplit(".", 1)[1]
+            e_idx = int(re.match(r"l\d+\.[se](\d+)\.", spec.name).group(1))
+            key = (proj, (layer * (cfg.n_experts + cfg.n_shared) + e_idx) % expert_pool)
+            if key not in pool:
+                src = replace_name(spec, f"pool.{key[1]}.{proj}")
+                a = synth.generate(src, cfg.seed)
+                pool[key] = (torch.from_numpy(a.codes).cuda(), torch.from_numpy(a.scales).cuda(), float(a.tensor_scale))
+            codes, scales, ts = pool[key]
+            d.dtype = mk.DTYPE["nvfp4"]
+            d.rows, d.cols = spec.shape
+            d.data, d.scales, d.tensor_scale = codes.data_ptr(), scales.data_ptr(), ts
+            t = None
+            n_fp4 += 1
+        else:
+            t = synth.generate_gpu(spec, cfg.seed)
+            d.dtype = mk.DTYPE["bf16"]
+            d.rows, d.cols = (1, spec.shape[0]) if len(spec.shape) == 1 else spec.shape
+            d.data = t.data_ptr()
         arr = (mk.WeightDesc * 1)(d)
         mk.check(m.lib.mk_load_weights(m.ctx, arr, 1, torch.cuda.current_stream().cuda_stream))
         torch.cuda.current_stream().synchronize()
         del t
+    del pool
     wcfg = cfg.with_batch(max_batch)
     for spec in synth.state_specs(wcfg):
         t = synth.generate_gpu(spec, cfg.seed)
         layer, kind = int(spec.name.split(".")[0][1:]), spec.name.split(".")[1]
-        dst = {"kcache": m.k_cache, "vcache": m.v_cache, "lstate": m.lin_state}[kind][layer]
+        dst = {"kcache": m.k_cache, "vcache": m.v_cache, "lstate": m.lin_state, "latent": m.latent}[kind][layer]
         dst.copy_(t)
         del t
     torch.cuda.synchronize()
     log(f"weights and states generated and packed in {time.time() - t0:.1f} s "
-        f"({m.sizes.packed_weights / 1e9:.2f} GB packed)")
+        f"({m.sizes.packed_weights / 1e9:.2f} GB packed"
+        + (f"; {n_fp4} NVFP4 matrices from a pool of {expert_pool} per projection" if n_fp4 else "") + ")")
     return m
 
 
+def replace_name(spec, name):
+    from dataclasses import replace
+
+    return replace(spec, name=name)
+
+
 def time_steps(m, cfg, batch, steps, warmup, perop=False):
+    """Times `steps` launches after `warmup` untimed ones with HIP events on the launch stream. A decode
+    step takes tokens (or hidden states) for `batch` sequences at position ctx; a verify step (the
+    configuration has verify rows) takes one anchor and seven drafts at position ctx. Returns the times
+    and, for mixture-of-experts layers, the size of the batch's expert union per layer in the last step."""
     import torch
 
     from persistent_megakernel_mk_amd import synth
 
-    toks = torch.from_numpy(synth.make_inputs(cfg.with_batch(batch))["tokens"]).cuda()
-    pos = [cfg.ctx] * batch
-    out = m.outputs(batch)
+    inp = synth.make_inputs(cfg.with_batch(batch))
+    verify = bool(cfg.verify_rows)
+    if verify:
+        # anchor + drafts: uniform tokens (the accepted count does not change the work of the step)
+        toks = torch.from_numpy(synth.uniform_int(cfg.seed, 77, cfg.verify_rows, cfg.vocab).astype("int32")).cuda()
+        out = m.outputs(cfg.verify_rows)
+        acc = torch.zeros(2, dtype=torch.int32, device="cuda")
+        run = lambda: m.verify(cfg.ctx, toks, out=out, acc=acc)  # noqa: E731
+    else:
+        pos = [cfg.ctx] * batch
+        out = m.outputs(batch)
+        route = m.route_outputs(batch) if m.n_moe else None
+        if cfg.vocab:
+            toks = torch.from_numpy(inp["tokens"]).cuda()
+            run = lambda: m.decode(pos, tokens=toks, out=out, perop=perop, route=route)  # noqa: E731
+        else:
+            hid = torch.from_numpy(inp["hidden_in"]).cuda()
+            run = lambda: m.decode(pos, hidden_in=hid, out=out, perop=perop, route=route)  # noqa: E731
     for _ in range(warmup):
-        m.decode(pos, tokens=toks, out=out, perop=perop)
+        run()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
-        m.decode(pos, tokens=toks, out=out, perop=perop)
+        run()
         ev[i][1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e3
@@ -84,8 +140,30 @@ def time_steps(m, cfg, batch, steps, warmup, perop=False):
     status = m.device_status()
     if status[0] != 0:
         raise RuntimeError(f"device status {status}")
+    union = None
+    if not verify and m.n_moe:
+        idx = route[0].cpu().numpy()  # [n_moe][rows][top_k]
+        union = [float(len(set(idx[l].reshape(-1).tolist()))) for l in range(idx.shape[0])]
     return {"mean_ms": statistics.fmean(per), "median_ms": statistics.median(per), "p10_ms": per[int(0.1 * (steps - 1))],
-            "p90_ms": per[int(0.9 * (steps - 1))], "wall_ms": wall}
+            "p90_ms": per[int(0.9 * (steps - 1))], "wall_ms": wall, "union": union}
+
+
+def describe(cfg, batch):
+    if cfg.name in ("c1", "c2"):
+        what = (f"hybrid 27B-class dense {'verify step (anchor + 7 drafts)' if cfg.verify_rows else 'decode step'}, "
+                f"{cfg.n_layers} layers (3 GDN : 1 GQA), hidden {cfg.hidden}, SwiGLU {cfg.ffn}, vocab {cfg.vocab}, "
+                f"{cfg.ctx}-token KV cache")
+    elif cfg.name == "c3":
+        what = (f"Kimi-class slice decode step, {cfg.n_layers} layers (3 KDA : 1 absorbed MLA), hidden {cfg.hidden}, "
+                f"MoE {cfg.n_experts} experts top-{cfg.top_k} + {cfg.n_shared} shared (bf16, ffn {cfg.expert_ffn}), "
+                f"{cfg.ctx}-token latent cache")
+    elif cfg.name == "c4":
+        what = (f"NVFP4-expert slice decode step, {cfg.n_layers} GQA layers, hidden {cfg.hidden}, MoE {cfg.n_experts} "
+                f"experts top-{cfg.top_k} + {cfg.n_shared} shared (NVFP4, ffn {cfg.expert_ffn}), {cfg.ctx}-token KV cache")
+    else:
+        what = f"{cfg.n_layers}-layer decode step, hidden {cfg.hidden}"
+    rows = f"{cfg.verify_rows} rows" if cfg.verify_rows else f"batch {batch}"
+    return f"{cfg.name}: {what}, {rows}"
 
 
 PHASE_NAMES = {1: "embed", 2: "product", 3: "delta-rule", 4: "attention", 5: "merge", 6: "final", 7: "hidden-out"}
@@ -214,7 +292,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c1")
-    ap.add_argument("--batches", default="1,8", help="first is the headline; others are reported alongside")
+    ap.add_argument("--batches", default=None,
+                    help="first is the headline; others are reported alongside (default: 1,8; 1 for the verify "
+                         "configuration c2; 8 for c3)")
     ap.add_argument("--no-perop", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--trace", action="store_true", help="print a per-phase breakdown of one traced step")
@@ -235,7 +315,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    batches = [int(b) for b in args.batches.split(",")]
+    default_batches = {"c2": "1", "c3": "8"}
+    batches = [int(b) for b in (args.batches or default_batches.get(args.config, "1,8")).split(",")]
     if args.calib_copy:
         src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -250,18 +331,21 @@ def main() -> int:
     results = {}
     for b in batches:
         r = time_steps(m, cfg, b, args.steps, args.warmup)
-        by = accounting.step_bytes(cfg, b, cfg.ctx)
-        r["tokens_s"] = b / (r["mean_ms"] / 1e3)
+        rows = cfg.verify_rows or 1
+        by = accounting.step_bytes(cfg, b, cfg.ctx, rows=rows, union=r["union"])
+        r["tokens_s"] = b * rows / (r["mean_ms"] / 1e3)
         r["alg_bytes"] = by["total"]
         r["alg_gbs"] = by["total"] / (r["mean_ms"] / 1e3) / 1e9
         results[b] = r
-        log(f"batch {b}: mean {r['mean_ms']:.3f} ms median {r['median_ms']:.3f} ms -> {r['tokens_s']:.1f} tok/s, "
-            f"{r['alg_gbs']:.0f} GB/s algorithmic ({100 * r['alg_gbs'] / accounting.HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+        log(f"{describe(cfg, b)}: mean {r['mean_ms']:.3f} ms median {r['median_ms']:.3f} ms -> {r['tokens_s']:.1f} "
+            f"{'rows' if cfg.verify_rows else 'tok'}/s, {r['alg_gbs']:.0f} GB/s algorithmic "
+            f"({100 * r['alg_gbs'] / accounting.HBM_PEAK_GBS:.1f}% of 8 TB/s, {by['total'] / 1e9:.3f} GB per step"
+            + (f", expert union per layer {r['union']}" if r["union"] else "") + ")")
     if args.trace:
         for b in batches:
             trace_step(m, cfg, b)
     perop = None
-    if not args.no_perop:
+    if not args.no_perop and not cfg.verify_rows:
         r = time_steps(m, cfg, batches[0], max(3, args.steps // 4), 2, perop=True)
         perop = {"ms_per_step": r["mean_ms"], "tokens_s": batches[0] / (r["mean_ms"] / 1e3),
                  "launches_per_step": m.sizes.n_phases}
@@ -270,7 +354,7 @@ def main() -> int:
     del m
     torch.cuda.empty_cache()
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and cfg.name == "c1":
         try:
             cpu = cpu_baseline(cfg)
             log(f"cpu oracle: {cpu['value']:.4f} tok/s on {cpu['cores']} threads ({cpu['sample']})")
@@ -290,10 +374,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded random weights, caches and states; tokens uniform)",
-        "config": {"workload": f"{cfg.name}: hybrid 27B-class dense decode step, {cfg.n_layers} layers "
-                               f"(3 GDN : 1 GQA), hidden {cfg.hidden}, SwiGLU {cfg.ffn}, vocab {cfg.vocab}, "
-                               f"{cfg.ctx}-token KV cache, batch {batches[0]}",
-                   "batch": batches[0], "kv_positions": cfg.ctx},
+        "config": {"workload": describe(cfg, batches[0]), "batch": batches[0], "kv_positions": cfg.ctx},
         "roofline": {"bound": "hbm", "achieved": round(h["alg_gbs"], 1), "peak": accounting.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["alg_gbs"] / accounting.HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic() if (cfg.name == "c1" and batches[0] == 1) else None,

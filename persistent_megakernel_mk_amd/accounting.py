@@ -11,6 +11,7 @@ are not counted.
 """
 from __future__ import annotations
 
+import re
 from typing import Dict
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
@@ -39,19 +40,45 @@ def roofline_floor_ms(bytes_per_token: float, devices: int, gbs_per_device: floa
     return bytes_per_token / (devices * gbs_per_device * 1e9) * 1e3
 
 
-def step_bytes(cfg, batch: int, position: int, rows: int = 1) -> Dict[str, float]:
-    """Algorithmic bytes of one decode step (rows = 1) or verify block (rows = 8, batch = 1) of a dense
-    bf16 configuration. `position` is the position of the (first) new token, so position cached rows are
-    read per sequence and kv head."""
+def expected_union(n_experts: int, top_k: int, tokens: int) -> float:
+    """Expected number of distinct experts selected by `tokens` independent uniform top-k draws."""
+    if n_experts <= 0:
+        return 0.0
+    return n_experts * (1.0 - (1.0 - top_k / n_experts) ** tokens)
+
+
+def _matrix_bytes(spec) -> float:
+    if spec.kind == "bf16":
+        return spec.numel * 2
+    if spec.kind == "nvfp4":  # E2M1 codes (half a byte) + one E4M3 scale per 16 values + the tensor scale
+        return spec.numel // 2 + spec.numel // 16 + 4
+    return 0
+
+
+def step_bytes(cfg, batch: int, position: int, rows: int = 1, union=None) -> Dict[str, float]:
+    """Algorithmic bytes of one decode step (rows = 1) or verify block (rows = 8, batch = 1).
+    `position` is the position of the (first) new token, so position cached rows are read per sequence
+    and kv head (or latent rows per sequence). Mixture-of-experts layers count the router, the shared
+    experts and each routed expert in the batch's union once: `union` gives the union size per MoE layer
+    (counted from the step's routing), else its expectation under uniform routing is used."""
     from persistent_megakernel_mk_amd import synth
 
-    w = 0
+    seqs = batch
+    toks = batch * rows
+    moe_layers = [l for l in range(cfg.n_layers) if cfg.ffns[l] == "moe"]
+    if union is None:
+        union = [expected_union(cfg.n_experts, cfg.top_k, toks)] * len(moe_layers)
+    union_of = dict(zip(moe_layers, union))
+    w = 0.0
     for s in synth.weight_specs(cfg):
         if s.name == "embed":
             continue  # only the gathered rows are read
-        w += s.numel * (2 if s.kind == "bf16" else 0)
-    seqs = batch
-    toks = batch * rows
+        m = re.match(r"l(\d+)\.e(\d+)\.", s.name)
+        if m:  # routed expert: counted through the union below
+            if int(m.group(2)) == 0:
+                w += union_of[int(m.group(1))] * _matrix_bytes(s)
+            continue
+        w += _matrix_bytes(s)
     emb = toks * cfg.hidden * 2 if cfg.vocab else toks * cfg.hidden * 4
     kv = lin = 0
     for l in range(cfg.n_layers):
@@ -59,11 +86,15 @@ def step_bytes(cfg, batch: int, position: int, rows: int = 1) -> Dict[str, float
         if m == "gqa":
             row = cfg.n_kv_heads * cfg.head_dim * 2  # one position of K (or V), bf16
             kv += seqs * 2 * (position * row) + toks * 2 * row
+        elif m == "mla":
+            row = (cfg.kv_rank + cfg.rope_dim) * 2  # one latent row, bf16
+            kv += seqs * position * row + toks * row
         elif m in ("gdn", "kda"):
             st = cfg.lin_heads * cfg.d_v * cfg.d_k * 4
-            lin += seqs * 2 * st
-            if rows > 1:
-                lin += rows * st  # one snapshot per verify row
+            if rows > 1:  # verify: the live state is read, one snapshot per row is written, and the
+                lin += seqs * st + rows * st  # commit selects a snapshot slot (nothing copied back)
+            else:
+                lin += seqs * 2 * st
     out = toks * cfg.vocab * 4 if cfg.vocab else toks * cfg.hidden * 4
     total = w + emb + kv + lin + out
     return {"weights": w, "embed": emb, "kv": kv, "lin_state": lin, "out": out, "total": total}

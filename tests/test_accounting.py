@@ -40,3 +40,37 @@ def test_step_bytes_hybrid_27b():
     assert 41.1e9 < b1["total"] < 41.4e9
     b8 = A.step_bytes(cfg, 8, cfg.ctx)
     assert b8["weights"] == b1["weights"] and b8["kv"] > 7 * b1["kv"]
+
+
+def test_expected_union_closed_forms():
+    assert abs(A.expected_union(384, 8, 1) - 8.0) < 1e-9  # one token selects exactly k experts
+    assert abs(A.expected_union(16, 16, 5) - 16.0) < 1e-12  # top-k = E touches every expert
+    assert round(A.expected_union(384, 8, 8), 1) == 59.5
+    assert round(A.expected_union(256, 8, 8), 1) == 57.4
+
+
+def test_step_bytes_expert_latent_and_verify_configs():
+    from persistent_megakernel_mk_amd import synth
+
+    c3 = synth.CONFIGS["c3"]
+    b = A.step_bytes(c3, 8, c3.ctx)
+    # latent cache: 4096 rows of (512 + 64) bf16 read per sequence, one row appended per token
+    assert b["kv"] == 8 * (4096 * 576 * 2 + 576 * 2)
+    assert b["lin_state"] == 3 * 8 * 2 * 32 * 128 * 128 * 4
+    assert 22.6e9 < b["total"] < 22.8e9
+    # a routed expert enters once per layer however many rows select it
+    one = A.step_bytes(c3, 8, c3.ctx, union=[1.0] * 4)
+    two = A.step_bytes(c3, 8, c3.ctx, union=[2.0] * 4)
+    assert two["weights"] - one["weights"] == 4 * 3 * 2048 * 7168 * 2
+    c4 = synth.CONFIGS["c4"]
+    n = 2048 * 6144
+    e = A.step_bytes(c4, 1, c4.ctx, union=[8.0] * 8)
+    f = A.step_bytes(c4, 1, c4.ctx, union=[9.0] * 8)
+    assert f["weights"] - e["weights"] == 8 * 3 * (n // 2 + n // 16 + 4)  # NVFP4: 0.5625 B per weight
+    assert 3.0e9 < A.step_bytes(c4, 1, c4.ctx)["total"] < 3.1e9
+    assert 11.8e9 < A.step_bytes(c4, 8, c4.ctx)["total"] < 12.0e9
+    c2 = synth.CONFIGS["c2"]
+    v = A.step_bytes(c2, 1, c2.ctx, rows=8)
+    st = 16 * 128 * 128 * 4
+    assert v["lin_state"] == 48 * (st + 8 * st)  # live state read once, eight snapshots written
+    assert v["out"] == 8 * 151936 * 4
