@@ -1466,7 +1466,20 @@ __device__ __forceinline__ void merge_phase(CArgs &a, const Phase &ph, char *sme
     const int row = u / nq, h = u % nq;
     const float *p = a.attn + ((size_t)row * nq + h) * NC * W;
     lds_barrier();
-    for (int i = tid; i < NC * W; i += kThreads) pl[i] = ld_c(p + i);
+    // the chunks' partials, eight loads per thread in flight before the first is stored
+    for (int i0 = tid; i0 < NC * W; i0 += 8 * kThreads) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = i0 + q * kThreads;
+        v[q] = i < NC * W ? ld_c(p + i) : 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = i0 + q * kThreads;
+        if (i < NC * W) pl[i] = v[q];
+      }
+    }
     lds_barrier();
     if (tid < 64) {  // one wave: global max and normaliser over chunks, in chunk order per lane
       float M = -INFINITY;
