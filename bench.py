@@ -98,17 +98,17 @@ def replace_name(spec, name):
     return replace(spec, name=name)
 
 
-def time_steps(m, cfg, batch, steps, warmup, perop=False):
-    """Times `steps` launches after `warmup` untimed ones with HIP events on the launch stream. A decode
-    step takes tokens (or hidden states) for `batch` sequences at position ctx; a verify step (the
-    configuration has verify rows) takes one anchor and seven drafts at position ctx. Returns the times
-    and, for mixture-of-experts layers, the size of the batch's expert union per layer in the last step."""
+def make_runner(m, cfg, batch, perop=False):
+    """A closure that launches one step of the configuration: a decode step for `batch` sequences
+    (tokens, or hidden states for slices without a vocabulary) at position ctx, or a verify step (anchor
+    + 7 drafts) when the configuration has verify rows. Returns (run, route buffers or None, verify)."""
     import torch
 
     from persistent_megakernel_mk_amd import synth
 
     inp = synth.make_inputs(cfg.with_batch(batch))
     verify = bool(cfg.verify_rows)
+    route = None
     if verify:
         # anchor + drafts: uniform tokens (the accepted count does not change the work of the step)
         toks = torch.from_numpy(synth.uniform_int(cfg.seed, 77, cfg.verify_rows, cfg.vocab).astype("int32")).cuda()
@@ -125,6 +125,17 @@ def time_steps(m, cfg, batch, steps, warmup, perop=False):
         else:
             hid = torch.from_numpy(inp["hidden_in"]).cuda()
             run = lambda: m.decode(pos, hidden_in=hid, out=out, perop=perop, route=route)  # noqa: E731
+    return run, route, verify
+
+
+def time_steps(m, cfg, batch, steps, warmup, perop=False):
+    """Times `steps` launches after `warmup` untimed ones with HIP events on the launch stream. A decode
+    step takes tokens (or hidden states) for `batch` sequences at position ctx; a verify step (the
+    configuration has verify rows) takes one anchor and seven drafts at position ctx. Returns the times
+    and, for mixture-of-experts layers, the size of the batch's expert union per layer in the last step."""
+    import torch
+
+    run, route, verify = make_runner(m, cfg, batch, perop)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -166,7 +177,8 @@ def describe(cfg, batch):
     return f"{cfg.name}: {what}, {rows}"
 
 
-PHASE_NAMES = {1: "embed", 2: "product", 3: "delta-rule", 4: "attention", 5: "merge", 6: "final", 7: "hidden-out"}
+PHASE_NAMES = {1: "embed", 2: "product", 3: "delta-rule", 4: "attention", 5: "merge", 6: "final", 7: "hidden-out",
+               8: "latent-attention", 9: "latent-merge"}
 
 
 def trace_step(m, cfg, batch):
@@ -181,9 +193,9 @@ def trace_step(m, cfg, batch):
     ph = m.phases(batch)
     buf = torch.zeros(len(ph) * G * 2, dtype=torch.int64, device="cuda")
     m.set_trace(buf)
-    toks = torch.from_numpy(synth.make_inputs(cfg.with_batch(batch))["tokens"]).cuda()
+    run, _, _ = make_runner(m, cfg, batch)
     for _ in range(2):
-        m.decode([cfg.ctx] * batch, tokens=toks)
+        run()
     torch.cuda.synchronize()
     m.set_trace(None)
     t = buf.cpu().numpy().reshape(len(ph), G, 2).astype(np.float64) / 100.0  # microseconds

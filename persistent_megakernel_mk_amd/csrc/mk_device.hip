@@ -539,90 +539,68 @@ __device__ __forceinline__ bool needs_finalise(const Phase &ph) {
   return ph.out == OUT_RESID || (ph.out == OUT_LOGITS && ph.S > 1);
 }
 
-// Finalisation of one tile by the sync wave: every lane sums (row, b) values of the tile over the
-// partials in partial order (plus the residual), four partials' loads in flight at a time;
+// Finalisation of one tile by the sync wave: every lane sums its (row, b) values of the tile over the
+// partials in partial order (plus the residual), with the loads of sixteen partials in flight at a time
+// (an expert down product has one partial per (expert, k-split), so a tile can have over a hundred);
 // device-coherent loads read the other contributors' partials (no cache invalidation). Stores the
 // residual and the tile's sums of squares, or the logits and the argmax candidate of each row (kept by
 // lane b).
 __device__ __forceinline__ void finalise_tiles(CArgs &a, const Phase &ph, int tile, int S_eff, int TN, float &best_v,
                                                int &best_i) {
-  const int nfin = 1;
+  constexpr int kFinBatch = 16;
   const int R = a.R, lane = threadIdx.x & 63;
   const float *pp = part_of(a, ph.dst_part);
   const size_t pstride = (size_t)R * TN;
   const bool resid = ph.out == OUT_RESID;
   int row_k[2], b_k[2];
   bool ok_k[2];
+  size_t off[2];  // element offsets within a partial (a valid dummy for lanes without a value)
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int idx = lane + 64 * k;
     ok_k[k] = idx < 16 * R;
     b_k[k] = ok_k[k] ? idx >> 4 : 0;  // lanes 16 b .. 16 b + 15: the tile's 16 rows of row b
     row_k[k] = idx & 15;
+    off[k] = ok_k[k] ? (size_t)b_k[k] * TN + tile * kTileRows + row_k[k] : 0;
   }
   float kb_v[2] = {-INFINITY, -INFINITY};  // logits: best of this lane's (row b_k) values
   int kb_i[2] = {0x7fffffff, 0x7fffffff};
-  for (int f0 = 0; f0 < nfin; f0 += 4) {
-    int tq[4];
-    float acc[4][2];
+  float acc[2] = {0.0f, 0.0f};
+  for (int s0 = 0; s0 < S_eff; s0 += kFinBatch) {
+    float t[kFinBatch][2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tq[q] = f0 + q < nfin ? tile : -1;
-      acc[q][0] = acc[q][1] = 0.0f;
+    for (int j = 0; j < kFinBatch; ++j) {
+      const float *ps = pp + (size_t)min(s0 + j, S_eff - 1) * pstride;  // in bounds past the last partial
+#pragma unroll
+      for (int k = 0; k < 2; ++k) t[j][k] = s0 + j < S_eff ? ld_c(ps + off[k]) : 0.0f;
     }
-    size_t off[4][2];  // element offsets (a valid dummy for lanes or tiles without a value)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int j = 0; j < kFinBatch; ++j)
+      if (s0 + j < S_eff) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
-        off[q][k] = (tq[q] >= 0 && ok_k[k]) ? (size_t)b_k[k] * TN + tq[q] * kTileRows + row_k[k] : 0;
-    // four partials of the eight values per round: 32 loads issued before the first add (in order)
-    for (int s0 = 0; s0 < S_eff; s0 += 4) {
-      float t[4][4][2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float *ps = pp + (size_t)min(s0 + j, S_eff - 1) * pstride;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int k = 0; k < 2; ++k) t[j][q][k] = ld_c(ps + off[q][k]);
+        for (int k = 0; k < 2; ++k) acc[k] += t[j][k];
       }
+  }
+  float xv[2];  // the residual values this tile updates (loaded together)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (s0 + j < S_eff) {
+  for (int k = 0; k < 2; ++k)
+    xv[k] = resid ? ld_c(a.x + (ok_k[k] ? (size_t)b_k[k] * a.H + tile * kTileRows + row_k[k] : 0)) : 0.0f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int k = 0; k < 2; ++k) acc[q][k] += t[j][q][k];
-        }
-    }
-    float xv[4][2];  // the residual values these tiles update (loaded together)
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        xv[q][k] = resid ? ld_c(a.x + ((tq[q] >= 0 && ok_k[k]) ? (size_t)b_k[k] * a.H + tq[q] * kTileRows + row_k[k] : 0)) : 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (tq[q] < 0) continue;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int n = tq[q] * kTileRows + row_k[k], b = b_k[k];
-        float v = acc[q][k];
-        if (resid) {
-          if (ok_k[k]) {
-            v += xv[q][k];
-            st_c(a.x + (size_t)b * a.H + n, v);
-          }
-          float q2 = ok_k[k] ? v * v : 0.0f;  // sum of squares over the tile's 16 rows (16 consecutive lanes)
-#pragma unroll
-          for (int o = 8; o >= 1; o >>= 1) q2 += __shfl_xor(q2, o);
-          if (ok_k[k] && row_k[k] == 0) st_c(a.ss + (size_t)b * (a.H / kTileRows) + tq[q], q2);
-        } else if (ok_k[k]) {
-          a.logits[(size_t)b * a.V + n] = v;
-          if (v > kb_v[k] || (v == kb_v[k] && n < kb_i[k])) { kb_v[k] = v; kb_i[k] = n; }
-        }
+  for (int k = 0; k < 2; ++k) {
+    const int n = tile * kTileRows + row_k[k], b = b_k[k];
+    float v = acc[k];
+    if (resid) {
+      if (ok_k[k]) {
+        v += xv[k];
+        st_c(a.x + (size_t)b * a.H + n, v);
       }
+      float q2 = ok_k[k] ? v * v : 0.0f;  // sum of squares over the tile's 16 rows (16 consecutive lanes)
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) q2 += __shfl_xor(q2, o);
+      if (ok_k[k] && row_k[k] == 0) st_c(a.ss + (size_t)b * (a.H / kTileRows) + tile, q2);
+    } else if (ok_k[k]) {
+      a.logits[(size_t)b * a.V + n] = v;
+      if (v > kb_v[k] || (v == kb_v[k] && n < kb_i[k])) { kb_v[k] = v; kb_i[k] = n; }
     }
   }
   if (!resid) {  // per row: the first maximum over the finalised tiles, kept by lane b
