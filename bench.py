@@ -159,6 +159,31 @@ def time_steps(m, cfg, batch, steps, warmup, perop=False):
             "p90_ms": per[int(0.9 * (steps - 1))], "wall_ms": wall, "union": union}
 
 
+def stream_read_gbs(gib: int = 8, reps: int = 10) -> float:
+    """HBM read rate a plain library kernel reaches on this GPU: row sums of a float32 [rows][4096] matrix
+    of `gib` GiB (each byte read once; the outputs are 1/4096 of the input), timed with HIP events; the
+    best of `reps` passes, in GB/s. Of the torch kernels tried (full sum, max, copy, column sums) this
+    one reads fastest. A practical ceiling to set the step kernel's rate against, beside the published
+    8 TB/s."""
+    import torch
+
+    x = torch.ones((gib << 28) // 4096, 4096, dtype=torch.float32, device="cuda")
+    x.sum(dim=1)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        x.sum(dim=1)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    n = x.numel() * 4
+    del x
+    torch.cuda.empty_cache()
+    return n / (best / 1e3) / 1e9
+
+
 def describe(cfg, batch):
     if cfg.name in ("c1", "c2"):
         what = (f"hybrid 27B-class dense {'verify step (anchor + 7 drafts)' if cfg.verify_rows else 'decode step'}, "
@@ -312,6 +337,7 @@ def main() -> int:
     ap.add_argument("--trace", action="store_true", help="print a per-phase breakdown of one traced step")
     ap.add_argument("--plain-launch", action="store_true",
                     help="ordinary (non-cooperative) launch of the same grid, for profilers")
+    ap.add_argument("--no-stream-ref", action="store_true", help="skip the plain read-rate reference")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of this many MiB (a counter calibration kernel)")
     args = ap.parse_args()
@@ -365,6 +391,11 @@ def main() -> int:
     m.close()
     del m
     torch.cuda.empty_cache()
+    stream = None
+    if not args.no_stream_ref:
+        stream = stream_read_gbs()
+        log(f"plain read reference (float32 row sums over 8 GiB): {stream:.0f} GB/s "
+            f"({100 * stream / accounting.HBM_PEAK_GBS:.1f}% of 8 TB/s)")
     cpu = None
     if not args.no_cpu and cfg.name == "c1":
         try:
@@ -392,6 +423,9 @@ def main() -> int:
                      "traffic": counter_traffic() if (cfg.name == "c1" and batches[0] == 1) else None,
                      "alg_bytes_per_launch": h["alg_bytes"], "kernel": "mk_step_kernel"},
         "cpu_baseline": cpu,
+        "stream_read_ref": None if stream is None else {
+            "gbs": round(stream, 1), "kind": "float32 row sums of an 8 GiB [rows][4096] matrix (torch), best of 10",
+            "step_frac_of_ref": round(h["alg_gbs"] / stream, 4)},
         "latency_ms": {"median": round(h["median_ms"], 4), "p10": round(h["p10_ms"], 4), "p90": round(h["p90_ms"], 4)},
         "batches": {str(b): {"ms_per_step": round(r["mean_ms"], 4), "tokens_s": round(r["tokens_s"], 2),
                              "alg_gbs": round(r["alg_gbs"], 1),
