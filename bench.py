@@ -316,7 +316,7 @@ def counter_traffic():
         return None
     info = json.loads(m.group(1))
     h = hashlib.sha256()
-    for f in ("mk_device.hip", "mk_host.cpp", "mk_internal.h"):
+    for f in ("mk_device.h", "mk_step.hip", "mk_step_nvfp4.hip", "mk_host.cpp", "mk_internal.h"):
         h.update(open(os.path.join(ROOT, "persistent_megakernel_mk_amd", "csrc", f), "rb").read())
     if h.hexdigest() != info.get("kernel_source_sha256"):
         return None

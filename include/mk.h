@@ -194,6 +194,11 @@ mk_status mk_set_trace(mk_ctx *ctx, void *device_buffer, int64_t bytes);
  * length, partial buffer, counter offset. Returns -1 on bad arguments. */
 int mk_debug_phase_count(const mk_ctx *ctx, int rows);
 int mk_debug_phase(const mk_ctx *ctx, int rows, int i, int32_t *out16);
+/* The whole descriptor of phase i (the library's internal layout, for host-side checks of the schedule):
+ * copies it to out when bytes is large enough; returns its size in bytes, or -1 on bad arguments. */
+int mk_debug_phase_bytes(const mk_ctx *ctx, int rows, int i, void *out, int bytes);
+/* Bytes of the packed weight buffer (as mk_query_sizes reports), or -1 for a NULL context. */
+int64_t mk_debug_packed_bytes(const mk_ctx *ctx);
 
 const char *mk_last_error(void);
 

@@ -1075,9 +1075,11 @@ mk_status mk_decode_step_perop(mk_ctx *c, const mk_step_io *io, int batch, int u
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(c->device));
   if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
-  ++c->epoch;
+  // one launch per phase: no grid barrier runs, so the barrier counters (and the epoch their targets
+  // are counted from) stay as they are; the next persistent step continues from the same epoch
   StepArgs a;
   fill_args(c, a, batch, 0, io);
+  a.epoch = c->epoch + 1;  // unused by one-phase launches (they wait at no grid barrier)
   const int n = a.n_phases;
   for (int p = 0; p < n; ++p) {
     a.phase_begin = p;
@@ -1140,5 +1142,14 @@ int mk_debug_phase(const mk_ctx *c, int rows, int i, int32_t *out16) {
   memcpy(out16, v, sizeof(v));
   return 0;
 }
+
+int mk_debug_phase_bytes(const mk_ctx *c, int rows, int i, void *out, int bytes) {
+  if (!c || rows < 1 || rows > kMaxRows || i < 0 || i >= (int)c->sched[rows].phases.size() || !out) return -1;
+  if (bytes < (int)sizeof(Phase)) return (int)sizeof(Phase);
+  memcpy(out, &c->sched[rows].phases[(size_t)i], sizeof(Phase));
+  return (int)sizeof(Phase);
+}
+
+int64_t mk_debug_packed_bytes(const mk_ctx *c) { return c ? c->packed_bytes : -1; }
 
 }  // extern "C"

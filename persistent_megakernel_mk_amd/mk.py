@@ -275,7 +275,37 @@ class Megakernel:
         return out
 
     # ---- steps ----------------------------------------------------------------------------
-    def _io(self, tokens, hidden_in, positions, logits, hidden_out, argmax, route=None):
+    def _check(self, name, t, shape, dtype):
+        """A device tensor the kernel reads or writes through a raw pointer: its shape, dtype, device
+        and layout must be exactly what the step assumes (a wrong one would be read or written past
+        its end)."""
+        import torch
+
+        if t is None:
+            return
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.device != self.device:
+            raise ValueError(f"{name} is on {t.device}, the context's device is {self.device}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def _io(self, rows, tokens, hidden_in, positions, logits, hidden_out, argmax, route=None):
+        import torch
+
+        cfg = self.cfg
+        self._check("tokens", tokens, (rows,), torch.int32)
+        self._check("hidden_in", hidden_in, (rows, cfg.hidden), torch.float32)
+        self._check("logits", logits, (rows, cfg.vocab), torch.float32)
+        self._check("hidden_out", hidden_out, (rows, cfg.hidden), torch.float32)
+        self._check("argmax", argmax, (rows,), torch.int32)
+        if route is not None:
+            self._check("route indices", route[0], (self.n_moe, rows, cfg.top_k), torch.int32)
+            self._check("route gates", route[1], (self.n_moe, rows, cfg.top_k), torch.float32)
         io = StepIO()
         if route is not None:
             io.route_idx = route[0].data_ptr()
@@ -315,7 +345,7 @@ class Megakernel:
         optional (indices, gates) pair from route_outputs()."""
         B = len(positions)
         logits, hidden_out, argmax = out if out is not None else self.outputs(B)
-        io = self._io(tokens, hidden_in, positions, logits, hidden_out, argmax, route)
+        io = self._io(B, tokens, hidden_in, positions, logits, hidden_out, argmax, route)
         if perop:
             check(self.lib.mk_decode_step_perop(self.ctx, ctypes.byref(io), B, 0, _stream_ptr(stream)))
         else:
@@ -327,7 +357,8 @@ class Megakernel:
 
         logits, _, argmax = out if out is not None else self.outputs(MK_VERIFY_ROWS)
         acc = acc if acc is not None else torch.zeros(2, dtype=torch.int32, device=self.device)
-        io = self._io(tokens, None, [position], logits, None, argmax)
+        io = self._io(MK_VERIFY_ROWS, tokens, None, [position], logits, None, argmax)
+        self._check("accepted/bonus", acc, (2,), torch.int32)
         check(self.lib.mk_verify_step(self.ctx, ctypes.byref(io), ctypes.c_void_p(acc.data_ptr()),
                                       ctypes.c_void_p(acc.data_ptr() + 4), _stream_ptr(stream)))
         return {"logits": logits, "argmax": argmax, "accepted_bonus": acc}
