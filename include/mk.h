@@ -156,6 +156,24 @@ mk_status mk_load_weights(mk_ctx *ctx, const mk_weight_desc *w, int n, void *hip
  * states, writes logits (and argmax) or hidden_out, and the MoE routing if requested. */
 mk_status mk_decode_step(mk_ctx *ctx, const mk_step_io *io, int batch, void *hip_stream);
 
+/* Size of the library-held device array of mk_decode_step_noalloc, one per GPU (64 MiB). */
+#define MK_NOALLOC_SCRATCH_BYTES (64ll << 20)
+
+/* The decode step of mk_decode_step for callers that cannot allocate device memory or hand over a
+ * workspace at step time: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, kernel and results as mk_decode_step (bit-identical outputs and state
+ * updates). The step's per-call working set (grid-barrier and finalise counters, residual stream,
+ * k-split partial sums, attention partials, argmax candidates) lives in a device array inside the
+ * library, MK_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library's code is loaded on that GPU
+ * and held until the process ends; the call allocates nothing. The context's constant tables (phase
+ * table, RoPE tables, cache pointers) and its device status word stay in its bound workspace.
+ * Each call clears that GPU's array with a fill kernel on hip_stream, then runs the step there; the
+ * array keeps the last call's contents, so calls that overlap on one GPU (any context, any stream)
+ * race and must be ordered by the caller. Errors: MK_E_CAPACITY when the working set at this batch
+ * exceeds the array, MK_E_STATE when the array's address was not taken at mk_create (device index
+ * 64 or above); otherwise those of mk_decode_step. */
+mk_status mk_decode_step_noalloc(mk_ctx *ctx, const mk_step_io *io, int batch, void *hip_stream);
+
 /* Speculative verify of one sequence (batch 1): rows j = 0..7 are io->tokens[j] at positions[0] + j.
  * Row j attends to positions 0..positions[0]+j and advances linear states one row at a time. Writes
  * logits [8][vocab] and argmax [8], the accepted draft count a in [0, 7] (longest prefix with

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -28,6 +29,30 @@ extern "C" __global__ void mk_repack_bf16(const uint16_t *src, int64_t rows, int
 extern "C" __global__ void mk_repack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
                                            int64_t row_off, int64_t dst_rows);
 extern "C" __global__ void mk_store_f32(float *dst, float v);
+
+// ---------------------------------------------------------------------------------------------
+// Library-held working memory of mk_decode_step_noalloc: one array per GPU, part of this code object
+// (no allocation call is ever made for it; the runtime reserves it when the code object is loaded on
+// a device and holds it until the process ends). It holds one step's per-call working set: barrier
+// and finalise counters, the residual stream, k-split partial sums, attention partials and argmax
+// candidates. On the host the name `scratch` only stands in for the array: it is never passed to a
+// kernel or a copy. Its device address is taken once per device, in mk_create with that device
+// current, and kept in g_noalloc_ptr.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int64_t kNoAllocBytes = MK_NOALLOC_SCRATCH_BYTES;
+constexpr int kNoAllocDevices = 64;
+uint8_t *g_noalloc_ptr[kNoAllocDevices] = {};
+std::mutex g_noalloc_mu;
+}  // namespace
+
+// Zero n 16-byte words (a fill kernel rather than hipMemsetAsync, so a caller may capture the call).
+extern "C" __global__ void mk_zero16(uint4 *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 extern "C" __global__ void mk_repack_bf16_headT(const uint16_t *src, int64_t heads, int64_t nope, int64_t rank, uint4 *dst);
 
 namespace {
@@ -831,6 +856,50 @@ mk_status launch_step(mk_ctx *c, StepArgs &a, hipStream_t st) {
   return MK_OK;
 }
 
+// Takes the device address of this device's library-held array (once per device; the device is current).
+mk_status noalloc_init(int device) {
+  if (device < 0 || device >= kNoAllocDevices) return MK_OK;  // mk_decode_step_noalloc then refuses
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (g_noalloc_ptr[device]) return MK_OK;
+  void *p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return fail(MK_E_HIP, "hipGetSymbolAddress of the library working memory: %s", hipGetErrorString(e));
+  g_noalloc_ptr[device] = static_cast<uint8_t *>(p);
+  return MK_OK;
+}
+
+// Byte offsets of one step's working set at R rows inside the library-held array (the same regions,
+// sized for R rather than for the context's largest row count, as the bound workspace holds).
+struct NoAllocLayout {
+  int64_t bar, fin, x, ss, part[3], mix, attn, cand, total;
+};
+
+NoAllocLayout noalloc_layout(const mk_ctx *c, int R) {
+  const mk_config &f = c->cfg;
+  const Schedule &s = c->sched[R];
+  const int H = f.hidden;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    int64_t o = off;
+    off = align_up(off + std::max<int64_t>(bytes, 0), 256);
+    return o;
+  };
+  int64_t attn = 0;
+  if (f.n_q_heads > 0) attn = std::max<int64_t>(attn, (int64_t)R * f.n_q_heads * s.n_chunks * (f.head_dim + 2));
+  if (s.mla_chunks > 0) attn = std::max<int64_t>(attn, (int64_t)R * f.mla_heads * s.mla_chunks * (f.kv_rank + 2));
+  NoAllocLayout L;
+  L.bar = take(9 * 128);
+  L.fin = take(((int64_t)c->n_resid * (H / kTileRows) + f.vocab / kTileRows) * 4);
+  L.x = take((int64_t)R * H * 4);
+  L.ss = take((int64_t)R * (H / kTileRows) * 4);
+  for (int i = 0; i < 3; ++i) L.part[i] = take(s.part_floats[i] * 4);
+  L.mix = take((int64_t)R * c->mix_stride * 4);
+  L.attn = take(attn * 4);
+  L.cand = take((int64_t)c->G * R * 2 * 4);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -878,6 +947,7 @@ mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
       delete c;
       return fail(MK_E_HIP, "step kernel cannot be resident (%d per CU): %s", nb, hipGetErrorString(e));
     }
+    if (mk_status s = noalloc_init(hip_device)) { delete c; return s; }
   }
   *out = c;
   return MK_OK;
@@ -1051,6 +1121,40 @@ mk_status mk_decode_step(mk_ctx *c, const mk_step_io *io, int batch, void *strea
   return launch_step(c, a, st);
 }
 
+mk_status mk_decode_step_noalloc(mk_ctx *c, const mk_step_io *io, int batch, void *stream) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  if (batch < 1 || batch > c->cfg.max_batch) return fail(MK_E_CAPACITY, "batch %d out of [1, %d]", batch, c->cfg.max_batch);
+  if (mk_status s = check_step(c, io, batch, batch, 1)) return s;
+  if (c->device >= kNoAllocDevices || !g_noalloc_ptr[c->device])
+    return fail(MK_E_STATE, "device %d has no library working memory", c->device);
+  const NoAllocLayout L = noalloc_layout(c, batch);
+  if (L.total > kNoAllocBytes)
+    return fail(MK_E_CAPACITY, "the step's working set at batch %d is %lld bytes; the library holds %lld per GPU", batch,
+                (long long)L.total, (long long)kNoAllocBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipSetDevice(c->device));
+  if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
+  uint8_t *base = g_noalloc_ptr[c->device];
+  // the previous call on this GPU left its counters and partials here: start from zeros, and count
+  // this call's barriers from epoch 1
+  const int64_t n16 = L.total / 16;
+  hipLaunchKernelGGL(mk_zero16, dim3((unsigned)std::min<int64_t>(1024, (n16 + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint4 *>(base), n16);
+  HIP_TRY(hipGetLastError());
+  StepArgs a;
+  fill_args(c, a, batch, 0, io);
+  a.epoch = 1;
+  a.bar = reinterpret_cast<uint32_t *>(base + L.bar);
+  a.fin = reinterpret_cast<uint32_t *>(base + L.fin);
+  a.x = reinterpret_cast<float *>(base + L.x);
+  a.ss = reinterpret_cast<float *>(base + L.ss);
+  for (int i = 0; i < 3; ++i) a.part[i] = reinterpret_cast<float *>(base + L.part[i]);
+  a.mix = reinterpret_cast<float *>(base + L.mix);
+  a.attn = reinterpret_cast<float *>(base + L.attn);
+  a.cand = reinterpret_cast<float *>(base + L.cand);
+  return launch_step(c, a, st);
+}
+
 mk_status mk_verify_step(mk_ctx *c, const mk_step_io *io, int32_t *d_accepted, int32_t *d_bonus, void *stream) {
   if (!c) return fail(MK_E_ARG, "ctx is NULL");
   if (c->cfg.vocab <= 0) return fail(MK_E_UNSUPPORTED, "verify needs a vocabulary (logits) configuration");
@@ -1106,7 +1210,7 @@ mk_status mk_read_device_status(mk_ctx *c, int32_t *status, int32_t *phase) {
 void mk_destroy(mk_ctx *c) {
   if (!c) return;
   for (auto &g : c->graph)
-    if (g) hipGraphExecDestroy(g);
+    if (g) (void)hipGraphExecDestroy(g);
   delete c;
 }
 

@@ -81,6 +81,7 @@ def load() -> ctypes.CDLL:
     L.mk_load_weights.argtypes, L.mk_load_weights.restype = [vp, P(WeightDesc), ctypes.c_int, vp], ctypes.c_int
     L.mk_decode_step.argtypes, L.mk_decode_step.restype = [vp, P(StepIO), ctypes.c_int, vp], ctypes.c_int
     L.mk_verify_step.argtypes, L.mk_verify_step.restype = [vp, P(StepIO), vp, vp, vp], ctypes.c_int
+    L.mk_decode_step_noalloc.argtypes, L.mk_decode_step_noalloc.restype = [vp, P(StepIO), ctypes.c_int, vp], ctypes.c_int
     L.mk_decode_step_perop.argtypes = [vp, P(StepIO), ctypes.c_int, ctypes.c_int, vp]
     L.mk_decode_step_perop.restype = ctypes.c_int
     L.mk_read_device_status.argtypes = [vp, P(i32), P(i32)]
@@ -340,14 +341,18 @@ class Megakernel:
         return (torch.full(shp, -1, dtype=torch.int32, device=self.device),
                 torch.zeros(shp, dtype=torch.float32, device=self.device))
 
-    def decode(self, positions, tokens=None, hidden_in=None, out=None, stream=None, perop: bool = False, route=None):
+    def decode(self, positions, tokens=None, hidden_in=None, out=None, stream=None, perop: bool = False, route=None,
+               noalloc: bool = False):
         """One decode step for len(positions) sequences. tokens/hidden_in are device tensors; route is an
-        optional (indices, gates) pair from route_outputs()."""
+        optional (indices, gates) pair from route_outputs(). perop runs the per-op baseline (one launch per
+        phase); noalloc runs the step on the library-held working memory (mk_decode_step_noalloc)."""
         B = len(positions)
         logits, hidden_out, argmax = out if out is not None else self.outputs(B)
         io = self._io(B, tokens, hidden_in, positions, logits, hidden_out, argmax, route)
         if perop:
             check(self.lib.mk_decode_step_perop(self.ctx, ctypes.byref(io), B, 0, _stream_ptr(stream)))
+        elif noalloc:
+            check(self.lib.mk_decode_step_noalloc(self.ctx, ctypes.byref(io), B, _stream_ptr(stream)))
         else:
             check(self.lib.mk_decode_step(self.ctx, ctypes.byref(io), B, _stream_ptr(stream)))
         return {"logits": logits, "hidden_out": hidden_out, "argmax": argmax, "route": route}
