@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
             "orc_topk": ([vp, i32, i32, vp, vp], None),
             "orc_silu_mul": ([vp, vp, i64, vp], None),
             "orc_argmax": ([vp, i64], i64),
+            "orc_residual_add": ([vp, vp, i64], None),
+            "orc_moe_accumulate": ([vp, vp, f32, i64], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -209,6 +211,23 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return h
 
 
+def residual_add(x: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """x + o, elementwise in fp32 (a new array)."""
+    out = _f32(x).copy()
+    o = _f32(o)
+    assert out.shape == o.shape
+    lib().orc_residual_add(_p(out), _p(o), out.size)
+    return out
+
+
+def moe_accumulate(acc: np.ndarray, y: np.ndarray, w: float) -> None:
+    """acc += w * y in place (acc fp32, contiguous)."""
+    assert acc.dtype == np.float32 and acc.flags["C_CONTIGUOUS"]
+    y = _f32(y)
+    assert acc.shape == y.shape
+    lib().orc_moe_accumulate(_p(acc), _p(y), float(w), acc.size)
+
+
 def argmax(x: np.ndarray) -> int:
     x = _f32(x)
     return int(lib().orc_argmax(_p(x), x.size))
@@ -239,9 +258,9 @@ def _ffn(cfg, W, l: int, y: np.ndarray, route_log: Optional[dict]) -> np.ndarray
         idxs[b], gws[b] = idx, gw
         acc = np.zeros(cfg.hidden, dtype=np.float32)
         for s in range(cfg.n_shared):
-            acc = acc + _swiglu(W, f"l{l}.s{s}.", y[b])
+            moe_accumulate(acc, _swiglu(W, f"l{l}.s{s}.", y[b]), 1.0)
         for t in range(cfg.top_k):
-            acc = acc + np.float32(gw[t]) * _swiglu(W, f"l{l}.e{int(idx[t])}.", y[b])
+            moe_accumulate(acc, _swiglu(W, f"l{l}.e{int(idx[t])}.", y[b]), float(gw[t]))
         out[b] = acc
     if route_log is not None:
         route_log[l] = (idxs, gws, z)
@@ -341,9 +360,9 @@ def _stack(cfg, W, S, x: np.ndarray, b_of_row, pos_of_row, snapshots=None, route
             o = _mla_rows(cfg, W, S, l, y, b_of_row, pos_of_row)
         else:
             raise ValueError(mx)
-        x = x + o
+        x = residual_add(x, o)
         y = rmsnorm(x, W[f"l{l}.ffn_norm"], cfg.eps)
-        x = x + _ffn(cfg, W, l, y, route_log)
+        x = residual_add(x, _ffn(cfg, W, l, y, route_log))
     return x
 
 

@@ -284,6 +284,19 @@ void orc_topk(const float* z, int E, int k, int* idx, float* gates) {
   for (int t = 0; t < k; ++t) gates[t] = gates[t] / total;
 }
 
+// ---- residual add and expert combine ---------------------------------------------------------
+// x <- x + o (one residual block's output added to the residual stream; page "Kimi K3's TPU
+// megakernel ...", section "How it maps onto a TPU v7": mixer then residual, FFN then residual)
+void orc_residual_add(float* x, const float* o, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) x[i] = x[i] + o[i];
+}
+
+// acc <- acc + w * y: one expert's output added with its gate weight (shared experts pass w = 1,
+// routed experts their normalised score; same page and section: shared expert, then routed experts)
+void orc_moe_accumulate(float* acc, const float* y, float w, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) acc[i] = acc[i] + w * y[i];
+}
+
 // ---- SwiGLU activation and argmax ------------------------------------------------------------
 // h = silu(g) * u with silu(t) = t / (1 + exp(-t))
 void orc_silu_mul(const float* g, const float* u, int64_t n, float* h) {

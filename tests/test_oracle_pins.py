@@ -207,18 +207,6 @@ def test_attention_uniform_and_grouping(oracle):
     assert np.allclose(o2[0], bf16_val(vc[0, 17]), atol=1e-5)
 
 
-def test_attention_matches_float64_softmax_on_permuted_cache(oracle):
-    # permuting cache positions permutes nothing in the result (softmax attention is a set function)
-    rng = np.random.default_rng(8)
-    d, L = 64, 40
-    kc, vc = _cache(rng, 1, L, d), _cache(rng, 1, L, d)
-    q = rng.standard_normal(d).astype(np.float32)
-    perm = rng.permutation(L)
-    o1 = oracle.attention(q, 1, d, kc, vc, L)
-    o2 = oracle.attention(q, 1, d, np.ascontiguousarray(kc[:, perm]), np.ascontiguousarray(vc[:, perm]), L)
-    assert np.allclose(o1, o2, rtol=1e-5, atol=1e-6)
-
-
 # ---- gated delta rule ---------------------------------------------------------------------------
 
 def _delta_matrix_form(S0, Q, K, V, A, beta):
