@@ -40,8 +40,6 @@ def build_gpu(cfg, max_batch, expert_pool=8):
     onto the E2M1 x E4M3 grid); to keep that bounded, each projection kind uses a pool of `expert_pool`
     distinct encoded matrices, assigned to the experts in turn. Every expert still has its own packed
     copy, so the bytes a step streams are those of distinct experts; only the values repeat."""
-    import re
-
     import torch
 
     from persistent_megakernel_mk_amd import mk, synth
@@ -55,11 +53,8 @@ def build_gpu(cfg, max_batch, expert_pool=8):
         d = mk.WeightDesc()
         d.layer, d.kind, d.expert = layer, kind, expert
         if spec.kind == "nvfp4":
-            proj = spec.name.rsplit(".", 1)[1]
-            e_idx = int(re.match(r"l\d+\.[se](\d+)\.", spec.name).group(1))
-            key = (proj, (layer * (cfg.n_experts + cfg.n_shared) + e_idx) % expert_pool)
+            key, src = pooled_source(cfg, spec, expert_pool)
             if key not in pool:
-                src = replace_name(spec, f"pool.{key[1]}.{proj}")
                 a = synth.generate(src, cfg.seed)
                 pool[key] = (torch.from_numpy(a.codes).cuda(), torch.from_numpy(a.scales).cuda(), float(a.tensor_scale))
             codes, scales, ts = pool[key]
@@ -90,6 +85,19 @@ def build_gpu(cfg, max_batch, expert_pool=8):
         f"({m.sizes.packed_weights / 1e9:.2f} GB packed"
         + (f"; {n_fp4} NVFP4 matrices from a pool of {expert_pool} per projection" if n_fp4 else "") + ")")
     return m
+
+
+def pooled_source(cfg, spec, expert_pool=8):
+    """The generator spec whose seeded values the NVFP4 expert matrix `spec` takes in build_gpu: per
+    projection kind, `expert_pool` distinct encoded matrices assigned to the experts in turn. Returns
+    (pool key, spec)."""
+    import re
+
+    layer = int(re.match(r"l(\d+)\.", spec.name).group(1))
+    proj = spec.name.rsplit(".", 1)[1]
+    e_idx = int(re.match(r"l\d+\.[se](\d+)\.", spec.name).group(1))
+    key = (proj, (layer * (cfg.n_experts + cfg.n_shared) + e_idx) % expert_pool)
+    return key, replace_name(spec, f"pool.{key[1]}.{proj}")
 
 
 def replace_name(spec, name):

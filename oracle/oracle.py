@@ -263,7 +263,7 @@ def _ffn(cfg, W, l: int, y: np.ndarray, route_log: Optional[dict]) -> np.ndarray
             moe_accumulate(acc, _swiglu(W, f"l{l}.e{int(idx[t])}.", y[b]), float(gw[t]))
         out[b] = acc
     if route_log is not None:
-        route_log[l] = (idxs, gws, z)
+        route_log[l] = (idxs, gws, z, y)  # y: the router's input, for the callers' rounding bounds
     return out
 
 
@@ -371,21 +371,26 @@ def embed(W, tokens: np.ndarray) -> np.ndarray:
     return widen(np.ascontiguousarray(E[np.asarray(tokens, dtype=np.int64)]))
 
 
-def decode_step(cfg, W, S: Dict[str, np.ndarray], inputs: Dict[str, np.ndarray], pos: int) -> dict:
-    """One decode step for ``cfg.batch`` sequences, all at position ``pos``. Caches and recurrent states
-    in ``S`` are updated in place. Returns logits and their argmax (vocabulary configs) or the final
-    hidden state (slice configs), plus per-layer routing for MoE layers."""
+def decode_step(cfg, W, S: Dict[str, np.ndarray], inputs: Dict[str, np.ndarray], pos) -> dict:
+    """One decode step for ``cfg.batch`` sequences at position ``pos`` (one int for all, or one per
+    sequence). Caches and recurrent states in ``S`` are updated in place. Returns logits and their argmax
+    (vocabulary configs) or the final hidden state (slice configs), plus per-layer routing for MoE
+    layers."""
     B = cfg.batch
+    positions = [int(p) for p in pos] if np.ndim(pos) else [int(pos)] * B
+    assert len(positions) == B
     if cfg.vocab:
         x = embed(W, inputs["tokens"])
     else:
         x = _f32(inputs["hidden_in"]).copy()
     route_log: dict = {}
-    x = _stack(cfg, W, S, x, list(range(B)), [pos] * B, route_log=route_log)
+    x = _stack(cfg, W, S, x, list(range(B)), positions, route_log=route_log)
     out = {"routes": route_log}
     if cfg.vocab:
-        logits = gemv(W["lm_head"], rmsnorm(x, W["final_norm"], cfg.eps))
+        y = rmsnorm(x, W["final_norm"], cfg.eps)
+        logits = gemv(W["lm_head"], y)
         out["logits"] = logits
+        out["final_y"] = y  # the LM head's input, for the callers' rounding bounds
         out["argmax"] = np.array([argmax(logits[b]) for b in range(B)], dtype=np.int32)
     else:
         out["hidden_out"] = x
@@ -404,14 +409,15 @@ def verify_step(cfg, W, S: Dict[str, np.ndarray], tokens: np.ndarray, pos: int) 
     x = embed(W, tokens)
     snapshots: dict = {}
     x = _stack(cfg, W, S, x, [0] * R, [pos + j for j in range(R)], snapshots=snapshots)
-    logits = gemv(W["lm_head"], rmsnorm(x, W["final_norm"], cfg.eps))
+    y = rmsnorm(x, W["final_norm"], cfg.eps)
+    logits = gemv(W["lm_head"], y)
     am = np.array([argmax(logits[j]) for j in range(R)], dtype=np.int32)
     a = 0
     while a < R - 1 and int(tokens[a + 1]) == int(am[a]):
         a += 1
     for l, snaps in snapshots.items():
         S[f"l{l}.lstate"][...] = snaps[a]
-    return {"logits": logits, "argmax": am, "accepted": a, "bonus": int(am[a]), "snapshots": snapshots}
+    return {"logits": logits, "argmax": am, "accepted": a, "bonus": int(am[a]), "snapshots": snapshots, "final_y": y}
 
 
 def copy_states(S: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:

@@ -47,10 +47,9 @@ def test_moe_slice_matches_oracle(torch_gpu, oracle, synth, name, batch):
     h = out["hidden_out"].cpu().numpy()
     e = H.rel_err(h, ref["hidden_out"])
     idx, w = (t.cpu().numpy() for t in out["route"])
-    exact = H.assert_routes(idx, w, ref["routes"], _moe_layers(cfg))
-    print(f"{name} B={batch}: hidden rel err {e:.2e}, {exact} routing decisions exact")
+    H.routes_parity(idx, w, ref, cfg, synth.LazyWeights(cfg), f"{name} B={batch}")
+    print(f"{name} B={batch}: hidden rel err {e:.2e}")
     assert e < H.REL_TOL
-    assert exact > 0
     H.compare_states(m.get_states(batch), S_ref, new_positions=[cfg.ctx])
 
 
@@ -77,7 +76,7 @@ def test_moe_consecutive_steps(torch_gpu, oracle, synth):
         e = H.rel_err(out["hidden_out"].cpu().numpy(), ref["hidden_out"])
         assert e < H.REL_TOL, (step, e)
         idx, w = (t.cpu().numpy() for t in route)
-        H.assert_routes(idx, w, ref["routes"], _moe_layers(cfg))
+        H.routes_parity(idx, w, ref, cfg, W, f"c4s step {step}")
     H.compare_states(m.get_states(2), S)
 
 
@@ -95,7 +94,7 @@ def test_kda_decode_matches_oracle(torch_gpu, oracle, synth, batch):
     e = H.rel_err(out["logits"].cpu().numpy(), ref["logits"])
     print(f"c1s_kda B={batch}: logits rel err {e:.2e}")
     assert e < H.REL_TOL
-    H.assert_argmax(out["argmax"].cpu().numpy(), ref["logits"], 8 * H.REL_TOL * float(np.max(np.abs(ref["logits"]))))
+    H.argmax_parity(out["argmax"].cpu().numpy(), ref, W, f"c1s_kda B={batch}")
     H.compare_states(m.get_states(batch), S, new_positions=[cfg.ctx])
 
 

@@ -47,8 +47,7 @@ def test_decode_matches_oracle(torch_gpu, oracle, synth, name, batch):
     e = H.rel_err(logits, ref["logits"])
     print(f"{name} B={batch}: logits rel err {e:.2e}")
     assert e < H.REL_TOL
-    tol_abs = 8 * H.REL_TOL * float(np.max(np.abs(ref["logits"])))
-    H.assert_argmax(out["argmax"].cpu().numpy(), ref["logits"], tol_abs)
+    H.argmax_parity(out["argmax"].cpu().numpy(), ref, synth.LazyWeights(cfg), f"{name} B={batch}")
     H.compare_states(m.get_states(batch), S_ref, new_positions=[cfg.ctx])
 
 

@@ -349,7 +349,7 @@ def test_moe_routes_to_the_selected_experts_only(oracle):
     y = rng.standard_normal((1, H)).astype(np.float32)
     log = {}
     out = oracle._ffn(_MoECfg(E, 2, H, F), W, 0, y, log)
-    idx, gw, z = log[0]
+    idx, gw, z, _ = log[0]
     top2 = np.argsort(-z[0], kind="stable")[:2]
     assert list(idx[0]) == list(top2)
     # zeroing an unselected expert changes nothing; zeroing a selected one does
