@@ -106,10 +106,48 @@ def replace_name(spec, name):
     return replace(spec, name=name)
 
 
-def make_runner(m, cfg, batch, perop=False):
+def save_states(m):
+    return {(k, l): t.clone() for k, d in (("k", m.k_cache), ("v", m.v_cache), ("s", m.lin_state), ("lat", m.latent))
+            for l, t in d.items()}
+
+
+def restore_states(m, saved):
+    for (k, l), t in saved.items():
+        {"k": m.k_cache, "v": m.v_cache, "s": m.lin_state, "lat": m.latent}[k][l].copy_(t)
+
+
+def seeded_drafts(m, cfg, p_greedy=0.8):
+    """The verify workload's block: an anchor token and seven drafts at positions ctx..ctx+7. Draft i is,
+    with probability p_greedy, the greedy (argmax) continuation of the anchor and drafts 1..i-1, else a
+    uniform token other than it; the choice continues to condition the later drafts. The uniforms and
+    the other tokens come from the seeded generator; the greedy tokens from decode steps of the same
+    context, whose states are restored afterwards. Then P(a >= i) = p_greedy^i for the accepted count a."""
+    import numpy as np
+    import torch
+
+    from persistent_megakernel_mk_amd import synth
+
+    n = cfg.verify_rows - 1
+    u = synth.draft_uniforms(cfg, n)
+    other = synth.draft_tokens_other(cfg, n)
+    toks = [int(synth.make_inputs(cfg.with_batch(1))["tokens"][0])]
+    saved = save_states(m)
+    out = m.outputs(1)
+    for i in range(n):
+        m.decode([cfg.ctx + i], tokens=torch.tensor(toks[i:i + 1], dtype=torch.int32, device="cuda"), out=out)
+        t = int(out[2][0].item())
+        toks.append(t if u[i] < p_greedy else int(other[i]) + (int(other[i]) >= t))
+    torch.cuda.synchronize()
+    restore_states(m, saved)
+    del saved
+    return np.array(toks, np.int32)
+
+
+def make_runner(m, cfg, batch, perop=False, drafts=None, graph=False):
     """A closure that launches one step of the configuration: a decode step for `batch` sequences
     (tokens, or hidden states for slices without a vocabulary) at position ctx, or a verify step (anchor
-    + 7 drafts) when the configuration has verify rows. Returns (run, route buffers or None, verify)."""
+    + 7 drafts, `drafts` or uniform tokens) when the configuration has verify rows. Returns (run, route
+    buffers or None, verify, verify outputs or None)."""
     import torch
 
     from persistent_megakernel_mk_amd import synth
@@ -117,11 +155,14 @@ def make_runner(m, cfg, batch, perop=False):
     inp = synth.make_inputs(cfg.with_batch(batch))
     verify = bool(cfg.verify_rows)
     route = None
+    vout = None
     if verify:
-        # anchor + drafts: uniform tokens (the accepted count does not change the work of the step)
-        toks = torch.from_numpy(synth.uniform_int(cfg.seed, 77, cfg.verify_rows, cfg.vocab).astype("int32")).cuda()
+        if drafts is None:
+            drafts = synth.uniform_int(cfg.seed, 77, cfg.verify_rows, cfg.vocab).astype("int32")
+        toks = torch.from_numpy(drafts).cuda()
         out = m.outputs(cfg.verify_rows)
         acc = torch.zeros(2, dtype=torch.int32, device="cuda")
+        vout = acc
         run = lambda: m.verify(cfg.ctx, toks, out=out, acc=acc)  # noqa: E731
     else:
         pos = [cfg.ctx] * batch
@@ -129,21 +170,30 @@ def make_runner(m, cfg, batch, perop=False):
         route = m.route_outputs(batch) if m.n_moe else None
         if cfg.vocab:
             toks = torch.from_numpy(inp["tokens"]).cuda()
-            run = lambda: m.decode(pos, tokens=toks, out=out, perop=perop, route=route)  # noqa: E731
+            run = lambda: m.decode(pos, tokens=toks, out=out, perop=perop, route=route, graph=graph)  # noqa: E731
         else:
             hid = torch.from_numpy(inp["hidden_in"]).cuda()
-            run = lambda: m.decode(pos, hidden_in=hid, out=out, perop=perop, route=route)  # noqa: E731
-    return run, route, verify
+            run = lambda: m.decode(pos, hidden_in=hid, out=out, perop=perop, route=route, graph=graph)  # noqa: E731
+    return run, route, verify, vout
 
 
-def time_steps(m, cfg, batch, steps, warmup, perop=False):
+def time_steps(m, cfg, batch, steps, warmup, perop=False, drafts=None, graph=False):
     """Times `steps` launches after `warmup` untimed ones with HIP events on the launch stream. A decode
     step takes tokens (or hidden states) for `batch` sequences at position ctx; a verify step (the
-    configuration has verify rows) takes one anchor and seven drafts at position ctx. Returns the times
-    and, for mixture-of-experts layers, the size of the batch's expert union per layer in the last step."""
+    configuration has verify rows) takes one anchor and seven drafts at position ctx. Returns the times,
+    for mixture-of-experts layers the size of the batch's expert union per layer in the last step, and
+    for verify the accepted count of the first (untimed) step from the context's initial states."""
     import torch
 
-    run, route, verify = make_runner(m, cfg, batch, perop)
+    run, route, verify, vout = make_runner(m, cfg, batch, perop, drafts, graph)
+    accepted = None
+    if verify:
+        saved = save_states(m)
+        run()
+        torch.cuda.synchronize()
+        accepted = int(vout[0].item())
+        restore_states(m, saved)
+        del saved
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -164,7 +214,7 @@ def time_steps(m, cfg, batch, steps, warmup, perop=False):
         idx = route[0].cpu().numpy()  # [n_moe][rows][top_k]
         union = [float(len(set(idx[l].reshape(-1).tolist()))) for l in range(idx.shape[0])]
     return {"mean_ms": statistics.fmean(per), "median_ms": statistics.median(per), "p10_ms": per[int(0.1 * (steps - 1))],
-            "p90_ms": per[int(0.9 * (steps - 1))], "wall_ms": wall, "union": union}
+            "p90_ms": per[int(0.9 * (steps - 1))], "wall_ms": wall, "union": union, "accepted": accepted}
 
 
 def stream_read_gbs(gib: int = 8, reps: int = 10) -> float:
@@ -226,7 +276,7 @@ def trace_step(m, cfg, batch):
     ph = m.phases(batch)
     buf = torch.zeros(len(ph) * G * 2, dtype=torch.int64, device="cuda")
     m.set_trace(buf)
-    run, _, _ = make_runner(m, cfg, batch)
+    run, _, _, _ = make_runner(m, cfg, batch)
     for _ in range(2):
         run()
     torch.cuda.synchronize()
@@ -262,10 +312,18 @@ def trace_step(m, cfg, batch):
     return agg
 
 
-def cpu_baseline(cfg_full, layers=4):
+def _omp_threads(n):
+    """Sets the OpenMP thread count of this process (the oracle's C++ ops run their output rows on it)."""
+    import ctypes
+
+    ctypes.CDLL("libgomp.so.1", mode=ctypes.RTLD_GLOBAL).omp_set_num_threads(int(n))
+
+
+def cpu_baseline(cfg_full, layers=4, repeats=3):
     """The CPU oracle, as it stands, on a bounded sample of the same workload: the first `layers` layers
-    (one full 3 GDN : 1 GQA group) plus the final norm and LM head, batch 1; the per-token time is
-    scaled to all layers as (layer time) * n_layers / layers + (head time)."""
+    (one full 3 GDN : 1 GQA group) plus the final norm and LM head, batch 1, timed `repeats` times with
+    all host threads and again with one thread (medians); the per-token time is scaled to all layers as
+    (layer time) * n_layers / layers + (head time)."""
     from dataclasses import replace
 
     import numpy as np
@@ -290,24 +348,37 @@ def cpu_baseline(cfg_full, layers=4):
     W._cache["embed"] = Rows(emb_spec, cfg.seed)
     for n in W.keys():
         W[n]
-    S = synth.make_states(cfg)
+    S0 = synth.make_states(cfg)
     inp = synth.make_inputs(cfg)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    # warm (page faults, thread pool), then time
-    S2 = O.copy_states(S)
-    O.decode_step(cfg, W, S2, inp, cfg.ctx)
-    t0 = time.perf_counter()
-    x = O.embed(W, inp["tokens"])
-    x = O._stack(cfg, W, S, x, [0], [cfg.ctx])
-    t1 = time.perf_counter()
-    logits = O.gemv(W["lm_head"], O.rmsnorm(x, W["final_norm"], cfg.eps))
-    O.argmax(logits[0])
-    t2 = time.perf_counter()
-    per_token = (t1 - t0) * cfg_full.n_layers / layers + (t2 - t1)
-    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {layers} of {cfg_full.n_layers} layers + final norm + LM head at batch 1, "
-                      f"{(t1 - t0):.2f} s for the layers and {(t2 - t1):.2f} s for the head, scaled to "
-                      f"{cfg_full.n_layers} layers ({per_token:.2f} s per token)"}
+    all_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def one_token():
+        S = O.copy_states(S0)
+        t0 = time.perf_counter()
+        x = O.embed(W, inp["tokens"])
+        x = O._stack(cfg, W, S, x, [0], [cfg.ctx])
+        t1 = time.perf_counter()
+        logits = O.gemv(W["lm_head"], O.rmsnorm(x, W["final_norm"], cfg.eps))
+        O.argmax(logits[0])
+        t2 = time.perf_counter()
+        return (t1 - t0) * cfg_full.n_layers / layers + (t2 - t1), t1 - t0, t2 - t1
+
+    res = {}
+    for threads in (all_threads, 1):
+        _omp_threads(threads)
+        one_token()  # warm (page faults, thread pool)
+        runs = sorted(one_token() for _ in range(repeats))
+        res[threads] = runs[len(runs) // 2]
+    _omp_threads(all_threads)
+    per, lay, head = res[all_threads]
+    per1, lay1, head1 = res[1]
+    return {"value": 1.0 / per, "unit": "tokens/s", "cores": all_threads, "kind": "oracle",
+            "sample": f"first {layers} of {cfg_full.n_layers} layers + final norm + LM head at batch 1, median of "
+                      f"{repeats}: {lay:.2f} s for the layers and {head:.2f} s for the head on {all_threads} threads, "
+                      f"scaled to {cfg_full.n_layers} layers ({per:.2f} s per token)",
+            "single_thread": {"value": 1.0 / per1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"same sample, median of {repeats}: {lay1:.2f} s layers + {head1:.2f} s head "
+                                        f"({per1:.2f} s per token)"}}
 
 
 def counter_traffic():
@@ -361,7 +432,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    default_batches = {"c2": "1", "c3": "8"}
+    default_batches = {"c0": "1", "c1": "1,2,4,8", "c2": "1", "c3": "8", "c4": "1,4,8"}
     batches = [int(b) for b in (args.batches or default_batches.get(args.config, "1,8")).split(",")]
     if args.calib_copy:
         src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")
@@ -374,9 +445,10 @@ def main() -> int:
     m = build_gpu(cfg, max(batches))
     if args.plain_launch:
         m.set_launch_mode(False)
+    drafts = seeded_drafts(m, cfg) if cfg.verify_rows else None
     results = {}
     for b in batches:
-        r = time_steps(m, cfg, b, args.steps, args.warmup)
+        r = time_steps(m, cfg, b, args.steps, args.warmup, drafts=drafts)
         rows = cfg.verify_rows or 1
         by = accounting.step_bytes(cfg, b, cfg.ctx, rows=rows, union=r["union"])
         r["tokens_s"] = b * rows / (r["mean_ms"] / 1e3)
@@ -386,16 +458,20 @@ def main() -> int:
         log(f"{describe(cfg, b)}: mean {r['mean_ms']:.3f} ms median {r['median_ms']:.3f} ms -> {r['tokens_s']:.1f} "
             f"{'rows' if cfg.verify_rows else 'tok'}/s, {r['alg_gbs']:.0f} GB/s algorithmic "
             f"({100 * r['alg_gbs'] / accounting.HBM_PEAK_GBS:.1f}% of 8 TB/s, {by['total'] / 1e9:.3f} GB per step"
-            + (f", expert union per layer {r['union']}" if r["union"] else "") + ")")
+            + (f", expert union per layer {r['union']}" if r["union"] else "")
+            + (f", accepted {r['accepted']} of 7 drafts -> {(r['accepted'] + 1) / (r['mean_ms'] / 1e3):.1f} emitted tok/s"
+               if r["accepted"] is not None else "") + ")")
     if args.trace:
         for b in batches:
             trace_step(m, cfg, b)
     perop = None
     if not args.no_perop and not cfg.verify_rows:
         r = time_steps(m, cfg, batches[0], max(3, args.steps // 4), 2, perop=True)
+        rg = time_steps(m, cfg, batches[0], max(3, args.steps // 4), 2, perop=True, graph=True)
         perop = {"ms_per_step": r["mean_ms"], "tokens_s": batches[0] / (r["mean_ms"] / 1e3),
-                 "launches_per_step": m.sizes.n_phases}
-        log(f"per-op baseline batch {batches[0]}: {r['mean_ms']:.3f} ms")
+                 "launches_per_step": m.sizes.n_phases,
+                 "graph": {"ms_per_step": rg["mean_ms"], "tokens_s": batches[0] / (rg["mean_ms"] / 1e3)}}
+        log(f"per-op baseline batch {batches[0]}: {r['mean_ms']:.3f} ms; as a HIP graph: {rg['mean_ms']:.3f} ms")
     m.close()
     del m
     torch.cuda.empty_cache()
@@ -424,7 +500,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded random weights, caches and states; tokens uniform)",
+        "data": "synthetic (seeded random weights, caches and states; tokens uniform"
+                + ("; drafts seeded, greedy with probability 0.8)" if cfg.verify_rows else ")"),
         "config": {"workload": describe(cfg, batches[0]), "batch": batches[0], "kv_positions": cfg.ctx},
         "roofline": {"bound": "hbm", "achieved": round(h["alg_gbs"], 1), "peak": accounting.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["alg_gbs"] / accounting.HBM_PEAK_GBS, 4),
@@ -441,6 +518,11 @@ def main() -> int:
                     for b, r in results.items()},
         "perop_baseline": perop,
     }
+    if h["accepted"] is not None:
+        line["verify"] = {"drafts": "seeded: each draft the greedy continuation with probability 0.8, else a uniform "
+                                    "other token", "tokens": [int(t) for t in drafts], "accepted": h["accepted"],
+                          "emitted_per_step": h["accepted"] + 1,
+                          "emitted_tokens_s": round((h["accepted"] + 1) / (h["mean_ms"] / 1e3), 2)}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -184,7 +184,10 @@ mk_status mk_verify_step(mk_ctx *ctx, const mk_step_io *io, int32_t *d_accepted,
 
 /* The same decode step as mk_decode_step, run as one kernel launch per phase (no persistent kernel,
  * no cross-phase prefetch): the non-fused baseline whose op boundaries the megakernel removes.
- * use_graph != 0 captures the launches in a HIP graph once per (batch) and replays it. */
+ * use_graph != 0 runs the same launches as one HIP graph: captured (on a stream of the context's own)
+ * the first time a row count is called with a given argument block, replayed on hip_stream by later
+ * calls with the same block (positions, tokens and output buffers); a call with another block captures
+ * again. The graph holds kernel launches only. */
 mk_status mk_decode_step_perop(mk_ctx *ctx, const mk_step_io *io, int batch, int use_graph, void *hip_stream);
 
 /* After the caller has synchronised the step's stream: *status is MK_OK or MK_E_DEVICE_TIMEOUT and

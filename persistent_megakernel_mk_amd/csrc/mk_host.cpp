@@ -142,9 +142,11 @@ struct mk_ctx {
   uint64_t *trace = nullptr;  // optional per-phase timestamps (device buffer)
   bool cooperative = true;    // cooperative launch (co-residency guaranteed by the runtime)
   bool nvfp4 = false;         // the schedule has NVFP4 products: the step kernel build that decodes them
-  // per-op baseline graphs
+  // per-op baseline graphs: one instantiated graph per row count, with the launch arguments it was
+  // captured with (a call whose arguments differ captures again), and the stream it is captured on
   hipGraphExec_t graph[kMaxRows + 1] = {};
-  const void *graph_key[kMaxRows + 1] = {};
+  StepArgs graph_args[kMaxRows + 1];
+  hipStream_t capture_stream = nullptr;
 };
 
 namespace {
@@ -1175,7 +1177,6 @@ mk_status mk_decode_step_perop(mk_ctx *c, const mk_step_io *io, int batch, int u
   if (!c) return fail(MK_E_ARG, "ctx is NULL");
   if (batch < 1 || batch > c->cfg.max_batch) return fail(MK_E_CAPACITY, "batch %d out of [1, %d]", batch, c->cfg.max_batch);
   if (mk_status s = check_step(c, io, batch, batch, 1)) return s;
-  if (use_graph) return fail(MK_E_UNSUPPORTED, "graph capture of the per-op baseline is not built yet");
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(c->device));
   if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
@@ -1183,15 +1184,41 @@ mk_status mk_decode_step_perop(mk_ctx *c, const mk_step_io *io, int batch, int u
   // are counted from) stay as they are; the next persistent step continues from the same epoch
   StepArgs a;
   fill_args(c, a, batch, 0, io);
-  a.epoch = c->epoch + 1;  // unused by one-phase launches (they wait at no grid barrier)
+  a.epoch = 1;  // unused by one-phase launches (they wait at no grid barrier); fixed, so graphs are reused
   const int n = a.n_phases;
-  for (int p = 0; p < n; ++p) {
-    a.phase_begin = p;
-    a.phase_end = p + 1;
-    a.barrier_base = p;
-    void *args[] = {&a};
-    HIP_TRY(hipLaunchKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
+  auto launch_all = [&](hipStream_t s) -> mk_status {
+    for (int p = 0; p < n; ++p) {
+      StepArgs ap = a;
+      ap.phase_begin = p;
+      ap.phase_end = p + 1;
+      ap.barrier_base = p;
+      void *args[] = {&ap};
+      HIP_TRY(hipLaunchKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, s));
+    }
+    return MK_OK;
+  };
+  if (!use_graph) return launch_all(st);
+  // the same launches as one HIP graph: captured on the context's own stream (the caller's may be the
+  // null stream, which cannot capture), instantiated once per row count and argument block, replayed
+  // on the caller's stream
+  if (!c->graph[batch] || memcmp(&c->graph_args[batch], &a, sizeof(StepArgs)) != 0) {
+    if (c->graph[batch]) {
+      HIP_TRY(hipGraphExecDestroy(c->graph[batch]));
+      c->graph[batch] = nullptr;
+    }
+    if (!c->capture_stream) HIP_TRY(hipStreamCreateWithFlags(&c->capture_stream, hipStreamNonBlocking));
+    HIP_TRY(hipStreamBeginCapture(c->capture_stream, hipStreamCaptureModeThreadLocal));
+    mk_status s = launch_all(c->capture_stream);
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(c->capture_stream, &g);
+    if (s != MK_OK) { if (g) (void)hipGraphDestroy(g); return s; }
+    if (e != hipSuccess) return fail(MK_E_HIP, "graph capture: %s", hipGetErrorString(e));
+    const hipError_t e2 = hipGraphInstantiate(&c->graph[batch], g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e2 != hipSuccess) { c->graph[batch] = nullptr; return fail(MK_E_HIP, "graph instantiate: %s", hipGetErrorString(e2)); }
+    c->graph_args[batch] = a;
   }
+  HIP_TRY(hipGraphLaunch(c->graph[batch], st));
   return MK_OK;
 }
 
@@ -1211,6 +1238,7 @@ void mk_destroy(mk_ctx *c) {
   if (!c) return;
   for (auto &g : c->graph)
     if (g) (void)hipGraphExecDestroy(g);
+  if (c->capture_stream) (void)hipStreamDestroy(c->capture_stream);
   delete c;
 }
 

@@ -342,15 +342,16 @@ class Megakernel:
                 torch.zeros(shp, dtype=torch.float32, device=self.device))
 
     def decode(self, positions, tokens=None, hidden_in=None, out=None, stream=None, perop: bool = False, route=None,
-               noalloc: bool = False):
+               noalloc: bool = False, graph: bool = False):
         """One decode step for len(positions) sequences. tokens/hidden_in are device tensors; route is an
         optional (indices, gates) pair from route_outputs(). perop runs the per-op baseline (one launch per
-        phase); noalloc runs the step on the library-held working memory (mk_decode_step_noalloc)."""
+        phase; with graph, replayed as a HIP graph); noalloc runs the step on the library-held working memory
+        (mk_decode_step_noalloc)."""
         B = len(positions)
         logits, hidden_out, argmax = out if out is not None else self.outputs(B)
         io = self._io(B, tokens, hidden_in, positions, logits, hidden_out, argmax, route)
         if perop:
-            check(self.lib.mk_decode_step_perop(self.ctx, ctypes.byref(io), B, 0, _stream_ptr(stream)))
+            check(self.lib.mk_decode_step_perop(self.ctx, ctypes.byref(io), B, int(graph), _stream_ptr(stream)))
         elif noalloc:
             check(self.lib.mk_decode_step_noalloc(self.ctx, ctypes.byref(io), B, _stream_ptr(stream)))
         else:

@@ -170,3 +170,36 @@ def test_persistent_and_per_op_steps_interleave_on_one_context(torch_gpu, oracle
         print(f"step {step} perop={perop}: logits rel err {e:.2e}")
         assert e < H.REL_TOL
     H.compare_states(mixed.get_states(2), S)
+
+
+def test_per_op_graph_replays_match_eager_launches(torch_gpu, oracle, synth):
+    """The per-op baseline replayed as a HIP graph: three replays of one graph (same position, tokens and
+    buffers; the linear states advance each time), with unrelated eager GPU work and synchronisations
+    between them, each bit-identical to the eager per-op launches on a second context, and the first
+    one within tolerance of the oracle."""
+    cfg = synth.CONFIGS["c1s"].with_batch(2)
+    W = synth.LazyWeights(cfg)
+    S = synth.make_states(cfg)
+    eager = H.make_gpu(cfg, W, S, max_batch=2)
+    graph = H.make_gpu(cfg, W, S, max_batch=2)
+    inp = synth.make_inputs(cfg)
+    t = torch_gpu.from_numpy(inp["tokens"]).cuda()
+    pos = [cfg.ctx] * 2
+    out_e, out_g = eager.outputs(2), graph.outputs(2)
+    ref = oracle.decode_step(cfg, W, S, inp, pos)
+    junk = torch_gpu.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        a = eager.decode(pos, tokens=t, out=out_e, perop=True)
+        b = graph.decode(pos, tokens=t, out=out_g, perop=True, graph=True)
+        junk = (junk * 1.0001 + 1.0).sin()  # eager work between replays
+        torch_gpu.cuda.synchronize()
+        assert eager.device_status() == (0, -1) and graph.device_status() == (0, -1)
+        assert torch_gpu.equal(a["logits"], b["logits"]), rep
+        assert torch_gpu.equal(a["argmax"], b["argmax"]), rep
+        if rep == 0:
+            e = H.rel_err(b["logits"].cpu().numpy(), ref["logits"])
+            print(f"graph replay 0: logits rel err {e:.2e}")
+            assert e < H.REL_TOL
+    sa, sb = eager.get_states(2), graph.get_states(2)
+    for k in sa:
+        assert np.array_equal(sa[k], sb[k]), k
