@@ -217,6 +217,48 @@ def time_steps(m, cfg, batch, steps, warmup, perop=False, drafts=None, graph=Fal
             "p90_ms": per[int(0.9 * (steps - 1))], "wall_ms": wall, "union": union, "accepted": accepted}
 
 
+def time_loop(m, cfg, batch, n, reps=5):
+    """Greedy decoding of n steps at positions ctx..ctx+n-1 two ways, both with the tokens staying on the
+    device: one mk_decode_loop launch (the kernel picks and re-embeds each token), and n separate step
+    launches each fed the previous step's argmax tensor. Median over `reps` of each, in ms per step."""
+    import torch
+
+    from persistent_megakernel_mk_amd import synth
+
+    toks = torch.from_numpy(synth.make_inputs(cfg.with_batch(batch))["tokens"]).cuda()
+    pos = [cfg.ctx] * batch
+    out = m.outputs(batch)
+    tout = torch.empty((n, batch), dtype=torch.int32, device="cuda")
+
+    def loop():
+        m.decode_loop(pos, toks, n, out=out, tokens_out=tout)
+
+    outs = [m.outputs(batch) for _ in range(n)]
+
+    def steps():
+        t = toks
+        for s in range(n):
+            m.decode([c + s for c in pos], tokens=t, out=outs[s])
+            t = outs[s][2]
+
+    res = {}
+    for name, fn in (("loop", loop), ("steps", steps)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / n)
+        res[name] = statistics.median(ts)
+    if m.device_status()[0] != 0:
+        raise RuntimeError(f"device status {m.device_status()}")
+    return res
+
+
 def stream_read_gbs(gib: int = 8, reps: int = 10) -> float:
     """HBM read rate a plain library kernel reaches on this GPU: row sums of a float32 [rows][4096] matrix
     of `gib` GiB (each byte read once; the outputs are 1/4096 of the input), timed with HIP events; the
@@ -412,6 +454,7 @@ def main() -> int:
                     help="first is the headline; others are reported alongside (default: 1,8; 1 for the verify "
                          "configuration c2; 8 for c3)")
     ap.add_argument("--no-perop", action="store_true")
+    ap.add_argument("--no-loop", action="store_true", help="skip the on-device multi-step loop measurement")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--trace", action="store_true", help="print a per-phase breakdown of one traced step")
     ap.add_argument("--plain-launch", action="store_true",
@@ -461,6 +504,12 @@ def main() -> int:
             + (f", expert union per layer {r['union']}" if r["union"] else "")
             + (f", accepted {r['accepted']} of 7 drafts -> {(r['accepted'] + 1) / (r['mean_ms'] / 1e3):.1f} emitted tok/s"
                if r["accepted"] is not None else "") + ")")
+    loop = None
+    if cfg.vocab and not cfg.verify_rows and not args.no_loop:
+        lr = time_loop(m, cfg, batches[0], 8)
+        loop = {"steps_per_launch": 8, "ms_per_step": round(lr["loop"], 4), "tokens_s": round(batches[0] / (lr["loop"] / 1e3), 2),
+                "separate_launches_ms_per_step": round(lr["steps"], 4)}
+        log(f"greedy decoding, 8 steps per launch: {lr['loop']:.3f} ms per step; as 8 launches: {lr['steps']:.3f} ms per step")
     if args.trace:
         for b in batches:
             trace_step(m, cfg, b)
@@ -517,6 +566,7 @@ def main() -> int:
                              "frac_of_peak": round(r["alg_gbs"] / accounting.HBM_PEAK_GBS, 4)}
                     for b, r in results.items()},
         "perop_baseline": perop,
+        "decode_loop": loop,
     }
     if h["accepted"] is not None:
         line["verify"] = {"drafts": "seeded: each draft the greedy continuation with probability 0.8, else a uniform "

@@ -156,6 +156,22 @@ mk_status mk_load_weights(mk_ctx *ctx, const mk_weight_desc *w, int n, void *hip
  * states, writes logits (and argmax) or hidden_out, and the MoE routing if requested. */
 mk_status mk_decode_step(mk_ctx *ctx, const mk_step_io *io, int batch, void *hip_stream);
 
+/* Most decode steps one mk_decode_loop launch runs. */
+#define MK_MAX_LOOP_STEPS 32
+
+/* n_steps greedy decode steps of `batch` sequences in one persistent kernel launch (the pages' on-device
+ * loop, page "Kimi K3's TPU megakernel: 92 layers in one Pallas call, and what 709 tokens a second
+ * measures", section "What DSpark changes per step": many steps inside one device call, so the host takes
+ * part once per call). Step 0 embeds io->tokens at io->positions[b]; step s > 0 embeds, at positions[b] + s,
+ * the token step s - 1 emitted: the argmax of its logits (first maximum), chosen and re-embedded inside the
+ * kernel with no host round trip. Each step appends its K/V (or latent) rows and advances the linear
+ * states exactly as mk_decode_step would. d_tokens_out: device int32 [n_steps][batch], the token each step
+ * emitted. io->logits and io->argmax receive the last step's. Needs a vocabulary configuration;
+ * 1 <= n_steps <= MK_MAX_LOOP_STEPS and positions[b] + n_steps <= max_ctx (else MK_E_CAPACITY). Calls on
+ * one context are ordered on one stream (the expanded phase table lives in the bound workspace). */
+mk_status mk_decode_loop(mk_ctx *ctx, const mk_step_io *io, int batch, int n_steps, int32_t *d_tokens_out,
+                         void *hip_stream);
+
 /* Size of the library-held device array of mk_decode_step_noalloc, one per GPU (64 MiB). */
 #define MK_NOALLOC_SCRATCH_BYTES (64ll << 20)
 

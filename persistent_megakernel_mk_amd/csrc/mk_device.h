@@ -92,6 +92,9 @@ __device__ __forceinline__ int pos_of(CArgs &a, int i) {
     if (i == k) p = a.pos[k];
   return p;
 }
+// position of sequence i's new token in the decode step phase ph belongs to (a multi-step launch
+// advances every sequence by one position per step)
+__device__ __forceinline__ int pos_at(CArgs &a, const Phase &ph, int i) { return pos_of(a, i) + ph.step; }
 
 // workgroup barrier that orders LDS only (global memory is ordered explicitly where needed)
 __device__ __forceinline__ void lds_barrier() {
@@ -1041,7 +1044,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
   for (int u = u0; u < u1; ++u) {
     const int row = u / (nkv * NC), g = (u / NC) % nkv, c = u % NC;
     const int seq = a.verify ? 0 : row;
-    const int pbase = pos_of(a, seq);
+    const int pbase = pos_at(a, ph, seq);
     const int prow = pbase + (a.verify ? row : 0);
     const int j0 = c * CS, j1 = min(j0 + CS, prow + 1);
     const size_t cbase = ((size_t)seq * nkv + g) * a.max_ctx;
@@ -1256,7 +1259,7 @@ __device__ __forceinline__ void mla_phase(CArgs &a, const Phase &ph, char *smem)
     // unit order (head group, row, chunk): the head groups of one (row, chunk) sit G/NHG apart
     const int hg = u / (R * NC), rc = u - hg * (R * NC), row = rc / NC, c = rc - row * NC;
     const int seq = a.verify ? 0 : row;
-    const int pbase = pos_of(a, seq);
+    const int pbase = pos_at(a, ph, seq);
     const int prow = pbase + (a.verify ? row : 0);  // this row attends positions 0 .. prow
     const int j0 = c * CS, j1 = min(j0 + CS, prow + 1);
     const int h0 = hg * HG;
@@ -1503,7 +1506,9 @@ __device__ __forceinline__ void embed_phase(CArgs &a, const Phase &ph, char *sme
       const int n = t * kTileRows + tid;
       float v;
       if (a.V > 0) {
-        int tok = a.tokens[row];
+        // the first step embeds the caller's tokens; a later step of a multi-step launch the token the
+        // previous step emitted (written by workgroup 0 before the grid barrier)
+        int tok = ph.step == 0 ? a.tokens[row] : ld_ci(a.loop_tokens + (size_t)(ph.step - 1) * a.R + row);
         if (tok < 0 || tok >= a.V) {  // out-of-range token: report, read row 0 instead of faulting
           if (tid == 0) { st_ci(a.status + 1, -2); st_ci(a.status + 0, 1 /* MK_E_ARG */); }
           tok = 0;
@@ -1523,7 +1528,7 @@ __device__ __forceinline__ void embed_phase(CArgs &a, const Phase &ph, char *sme
   }
 }
 
-__device__ __forceinline__ void final_phase(CArgs &a, char *smem) {
+__device__ __forceinline__ void final_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, G = gridDim.x, tid = threadIdx.x;
   float *cv = reinterpret_cast<float *>(smem);
   int *ci = reinterpret_cast<int *>(cv + G * kMaxRows);
@@ -1545,6 +1550,7 @@ __device__ __forceinline__ void final_phase(CArgs &a, char *smem) {
       }
       am[tid] = bi;
       if (blockIdx.x == 0 && a.argmax) a.argmax[tid] = bi;
+      if (blockIdx.x == 0 && a.loop_tokens) st_ci(a.loop_tokens + (size_t)ph.step * R + tid, bi);
     }
     lds_barrier();
   }
@@ -1594,7 +1600,7 @@ __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *sm
     case PH_MERGE:
     case PH_MLA_MERGE: merge_phase(a, ph, smem); break;
     case PH_MLA: mla_phase(a, ph, smem); break;
-    case PH_FINAL: final_phase(a, smem); break;
+    case PH_FINAL: final_phase(a, ph, smem); break;
     case PH_HIDDEN_OUT: hidden_out_phase(a); break;
     default: break;
   }
@@ -1617,7 +1623,7 @@ __device__ __forceinline__ void step_body(char *smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   int route_q = -1;  // expert gate/up phase whose routing this workgroup holds in LDS
   if (wave == kSyncWave) {
-    uint32_t k = (ap->epoch - 1u) * (uint32_t)ap->n_barriers + (uint32_t)ap->barrier_base;
+    uint32_t k = ap->bar_done + (uint32_t)ap->barrier_base;
     for (int p = ap->phase_begin; p < ap->phase_end; ++p) {
       CArgs &a = *ap;
       const Phase ph = load_phase(a, p);

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -129,7 +130,7 @@ struct mk_ctx {
   int mix_stride = 0;
   Schedule sched[kMaxRows + 1];  // by row count
   // scratch layout (byte offsets)
-  int64_t o_rope_mla = 0;
+  int64_t o_rope_mla = 0, o_loop = 0;
   int64_t o_status = 0, o_bar = 0, o_fin = 0, o_x = 0, o_ss = 0, o_part[3] = {0, 0, 0}, o_mix = 0, o_attn = 0,
           o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxRows + 1] = {}, scratch_bytes = 0;
   int64_t kv_bytes = 0, lin_bytes = 0, latent_bytes = 0;
@@ -137,7 +138,10 @@ struct mk_ctx {
   bool bound = false;
   uint8_t *wbuf = nullptr, *scratch = nullptr;
   mk_buffers bufs;
-  uint32_t epoch = 0;
+  uint32_t bar_done = 0;  // grid barriers completed on the bound workspace's counters (they are monotone)
+  // multi-step launches: expanded phase tables by (rows, steps), and which one the workspace holds
+  std::map<std::pair<int, int>, std::vector<Phase>> loop_tables;
+  std::pair<int, int> loop_loaded = {0, 0};
   bool needs_reset = false;
   uint64_t *trace = nullptr;  // optional per-phase timestamps (device buffer)
   bool cooperative = true;    // cooperative launch (co-residency guaranteed by the runtime)
@@ -627,6 +631,9 @@ mk_status scratch_layout(mk_ctx *c) {
   c->o_ptrs = take((int64_t)5 * MK_MAX_LAYERS * 8);
   for (int r = 1; r <= kMaxRows; ++r)
     if (!c->sched[r].phases.empty()) c->o_phases[r] = take((int64_t)c->sched[r].phases.size() * sizeof(Phase));
+  int64_t max_phases = 0;
+  for (int r = 1; r <= kMaxRows; ++r) max_phases = std::max<int64_t>(max_phases, (int64_t)c->sched[r].phases.size());
+  c->o_loop = take(f.vocab > 0 ? (int64_t)MK_MAX_LOOP_STEPS * max_phases * sizeof(Phase) : 0);  // multi-step tables
   c->scratch_bytes = off;
   c->kv_bytes = (int64_t)f.max_batch * f.n_kv_heads * f.max_ctx * f.head_dim * 2;
   c->lin_bytes = (int64_t)f.max_batch * f.lin_heads * f.d_v * f.d_k * 4;
@@ -759,7 +766,7 @@ void fill_args(mk_ctx *c, StepArgs &a, int R, int verify, const mk_step_io *io) 
   a.phases = reinterpret_cast<const Phase *>(c->scratch + c->o_phases[R]);
   a.n_phases = (int)sc.phases.size();
   a.n_barriers = a.n_phases - 1;
-  a.epoch = c->epoch;
+  a.bar_done = c->bar_done;
   a.R = R;
   a.verify = verify;
   a.phase_begin = 0;
@@ -839,7 +846,7 @@ mk_status reset_counters(mk_ctx *c, hipStream_t st) {
   HIP_TRY(hipMemsetAsync(c->scratch + c->o_status, 0, 256, st));
   HIP_TRY(hipMemsetAsync(c->scratch + c->o_bar, 0, 9 * 128, st));
   HIP_TRY(hipMemsetAsync(c->scratch + c->o_fin, 0, ((size_t)c->n_resid * (c->cfg.hidden / kTileRows) + c->cfg.vocab / kTileRows) * 4, st));
-  c->epoch = 0;
+  c->bar_done = 0;
   c->needs_reset = false;
   return MK_OK;
 }
@@ -856,6 +863,30 @@ mk_status launch_step(mk_ctx *c, StepArgs &a, hipStream_t st) {
     HIP_TRY(hipLaunchKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
   }
   return MK_OK;
+}
+
+// The phase table of a launch that runs n decode steps: n copies of the one-step table, each phase
+// tagged with its step; the weight stream's link from a step's last product phase (and the phases after
+// it) continues into the next step's first product phase, so the weights of step s + 1 are in flight
+// while step s finishes; routing owners are re-indexed into their copy.
+std::vector<Phase> loop_table(const Schedule &sc, int n) {
+  const int P = (int)sc.phases.size();
+  int first_gemv = -1;
+  for (int i = 0; i < P && first_gemv < 0; ++i)
+    if (sc.phases[(size_t)i].type == PH_GEMV) first_gemv = i;
+  std::vector<Phase> out;
+  out.reserve((size_t)n * P);
+  for (int s = 0; s < n; ++s) {
+    for (int i = 0; i < P; ++i) {
+      Phase ph = sc.phases[(size_t)i];
+      ph.step = s;
+      if (ph.next_gemv >= 0) ph.next_gemv += s * P;
+      else if (s + 1 < n && first_gemv >= 0) ph.next_gemv = first_gemv + (s + 1) * P;
+      if (ph.seg == SEG_EXPERT) ph.route_q += s * P;
+      out.push_back(ph);
+    }
+  }
+  return out;
 }
 
 // Takes the device address of this device's library-held array (once per device; the device is current).
@@ -984,6 +1015,7 @@ mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
   c->bufs = *b;
   c->wbuf = static_cast<uint8_t *>(b->packed_weights);
   c->scratch = static_cast<uint8_t *>(b->scratch);
+  c->loop_loaded = {0, 0};
   HIP_TRY(hipMemset(c->wbuf, 0, (size_t)c->packed_bytes));  // padding rows of fused matrices are zero
   HIP_TRY(hipMemset(c->scratch, 0, (size_t)c->scratch_bytes));
   // per-layer state pointers
@@ -1025,7 +1057,7 @@ mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
     if (s.phases.empty()) continue;
     HIP_TRY(hipMemcpy(c->scratch + c->o_phases[r], s.phases.data(), s.phases.size() * sizeof(Phase), hipMemcpyHostToDevice));
   }
-  c->epoch = 0;
+  c->bar_done = 0;
   c->bound = true;
   c->global_have = 0;
   for (auto &s : c->L) {
@@ -1117,9 +1149,39 @@ mk_status mk_decode_step(mk_ctx *c, const mk_step_io *io, int batch, void *strea
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(c->device));
   if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
-  ++c->epoch;
   StepArgs a;
   fill_args(c, a, batch, 0, io);
+  c->bar_done += (uint32_t)a.n_barriers;
+  return launch_step(c, a, st);
+}
+
+mk_status mk_decode_loop(mk_ctx *c, const mk_step_io *io, int batch, int n_steps, int32_t *d_tokens_out, void *stream) {
+  if (!c) return fail(MK_E_ARG, "ctx is NULL");
+  if (c->cfg.vocab <= 0) return fail(MK_E_UNSUPPORTED, "a decode loop samples tokens: it needs a vocabulary configuration");
+  if (batch < 1 || batch > c->cfg.max_batch) return fail(MK_E_CAPACITY, "batch %d out of [1, %d]", batch, c->cfg.max_batch);
+  if (n_steps < 1 || n_steps > MK_MAX_LOOP_STEPS) return fail(MK_E_CAPACITY, "n_steps %d out of [1, %d]", n_steps, MK_MAX_LOOP_STEPS);
+  if (!d_tokens_out) return fail(MK_E_ARG, "tokens_out is required");
+  if (mk_status s = check_step(c, io, batch, batch, n_steps)) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(hipSetDevice(c->device));
+  if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
+  const std::pair<int, int> key(batch, n_steps);
+  auto it = c->loop_tables.find(key);
+  if (it == c->loop_tables.end()) it = c->loop_tables.emplace(key, loop_table(c->sched[batch], n_steps)).first;
+  if (c->loop_loaded != key) {  // ordered on the stream before this launch (and after earlier ones)
+    HIP_TRY(hipMemcpyAsync(c->scratch + c->o_loop, it->second.data(), it->second.size() * sizeof(Phase),
+                           hipMemcpyHostToDevice, st));
+    c->loop_loaded = key;
+  }
+  StepArgs a;
+  fill_args(c, a, batch, 0, io);
+  a.phases = reinterpret_cast<const Phase *>(c->scratch + c->o_loop);
+  a.n_phases = (int)it->second.size();
+  a.n_barriers = a.n_phases - 1;
+  a.phase_end = a.n_phases;
+  a.loop_tokens = d_tokens_out;
+  a.trace = nullptr;  // a trace buffer is sized for one step
+  c->bar_done += (uint32_t)a.n_barriers;
   return launch_step(c, a, st);
 }
 
@@ -1138,14 +1200,14 @@ mk_status mk_decode_step_noalloc(mk_ctx *c, const mk_step_io *io, int batch, voi
   if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
   uint8_t *base = g_noalloc_ptr[c->device];
   // the previous call on this GPU left its counters and partials here: start from zeros, and count
-  // this call's barriers from epoch 1
+  // this call's barriers from zero
   const int64_t n16 = L.total / 16;
   hipLaunchKernelGGL(mk_zero16, dim3((unsigned)std::min<int64_t>(1024, (n16 + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<uint4 *>(base), n16);
   HIP_TRY(hipGetLastError());
   StepArgs a;
   fill_args(c, a, batch, 0, io);
-  a.epoch = 1;
+  a.bar_done = 0;
   a.bar = reinterpret_cast<uint32_t *>(base + L.bar);
   a.fin = reinterpret_cast<uint32_t *>(base + L.fin);
   a.x = reinterpret_cast<float *>(base + L.x);
@@ -1165,9 +1227,9 @@ mk_status mk_verify_step(mk_ctx *c, const mk_step_io *io, int32_t *d_accepted, i
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(c->device));
   if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
-  ++c->epoch;
   StepArgs a;
   fill_args(c, a, kMaxRows, 1, io);
+  c->bar_done += (uint32_t)a.n_barriers;
   a.accepted = d_accepted;
   a.bonus = d_bonus;
   return launch_step(c, a, st);
@@ -1180,11 +1242,11 @@ mk_status mk_decode_step_perop(mk_ctx *c, const mk_step_io *io, int batch, int u
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(hipSetDevice(c->device));
   if (c->needs_reset) { if (mk_status s = reset_counters(c, st)) return s; }
-  // one launch per phase: no grid barrier runs, so the barrier counters (and the epoch their targets
-  // are counted from) stay as they are; the next persistent step continues from the same epoch
+  // one launch per phase: no grid barrier runs, so the barrier counters (and the count of completed
+  // barriers their targets start from) stay as they are for the next persistent step
   StepArgs a;
   fill_args(c, a, batch, 0, io);
-  a.epoch = 1;  // unused by one-phase launches (they wait at no grid barrier); fixed, so graphs are reused
+  a.bar_done = 0;  // unused by one-phase launches (they wait at no grid barrier); fixed, so graphs are reused
   const int n = a.n_phases;
   auto launch_all = [&](hipStream_t s) -> mk_status {
     for (int p = 0; p < n; ++p) {

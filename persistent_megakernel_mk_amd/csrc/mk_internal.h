@@ -100,14 +100,14 @@ struct Phase {
   int32_t dkv_off, kr_off;              // offsets of the new latent and rotary key in the projection
   int32_t heads, hgroup;                // query heads, heads per unit
   int32_t mla_src;                      // partial buffer of the absorbed queries
-  int32_t pad2;
+  int32_t step;       // decode step of a multi-step launch this phase belongs to (0 in a one-step table)
 };
 
 struct StepArgs {
   const Phase *phases;
   int32_t n_phases;
   int32_t n_barriers;  // grid barriers per step
-  uint32_t epoch;      // 1-based step counter of this context (targets of monotone counters)
+  uint32_t bar_done;   // grid barriers completed on these counters before this launch (they are monotone)
   int32_t R;           // rows in this step: batch, or 8 for verify
   int32_t verify;
   int32_t phase_begin, phase_end;  // phases run by this launch (all, or one for the per-op baseline)
@@ -142,6 +142,8 @@ struct StepArgs {
   float *route_w;
   int32_t *accepted;
   int32_t *bonus;
+  int32_t *loop_tokens;  // multi-step launch: [steps][R] token emitted by each step (its argmax), which the
+                         // next step embeds; null for one step
   // config scalars
   int32_t H, V, max_ctx, mix_stride;
   int32_t nq, nkv, hd;

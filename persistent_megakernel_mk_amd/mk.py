@@ -82,6 +82,8 @@ def load() -> ctypes.CDLL:
     L.mk_decode_step.argtypes, L.mk_decode_step.restype = [vp, P(StepIO), ctypes.c_int, vp], ctypes.c_int
     L.mk_verify_step.argtypes, L.mk_verify_step.restype = [vp, P(StepIO), vp, vp, vp], ctypes.c_int
     L.mk_decode_step_noalloc.argtypes, L.mk_decode_step_noalloc.restype = [vp, P(StepIO), ctypes.c_int, vp], ctypes.c_int
+    L.mk_decode_loop.argtypes = [vp, P(StepIO), ctypes.c_int, ctypes.c_int, vp, vp]
+    L.mk_decode_loop.restype = ctypes.c_int
     L.mk_decode_step_perop.argtypes = [vp, P(StepIO), ctypes.c_int, ctypes.c_int, vp]
     L.mk_decode_step_perop.restype = ctypes.c_int
     L.mk_read_device_status.argtypes = [vp, P(i32), P(i32)]
@@ -357,6 +359,22 @@ class Megakernel:
         else:
             check(self.lib.mk_decode_step(self.ctx, ctypes.byref(io), B, _stream_ptr(stream)))
         return {"logits": logits, "hidden_out": hidden_out, "argmax": argmax, "route": route}
+
+    def decode_loop(self, positions, tokens, n_steps: int, out=None, tokens_out=None, stream=None):
+        """n_steps greedy decode steps in one launch: step s runs at positions[b] + s on the token step s - 1
+        emitted (its argmax), step 0 on `tokens`. Returns the emitted tokens [n_steps][B] and the last
+        step's logits and argmax."""
+        import torch
+
+        B = len(positions)
+        logits, hidden_out, argmax = out if out is not None else self.outputs(B)
+        if tokens_out is None:
+            tokens_out = torch.empty((n_steps, B), dtype=torch.int32, device=self.device)
+        self._check("tokens_out", tokens_out, (n_steps, B), torch.int32)
+        io = self._io(B, tokens, None, positions, logits, hidden_out, argmax)
+        check(self.lib.mk_decode_loop(self.ctx, ctypes.byref(io), B, int(n_steps), tokens_out.data_ptr(),
+                                      _stream_ptr(stream)))
+        return {"tokens": tokens_out, "logits": logits, "argmax": argmax}
 
     def verify(self, position: int, tokens, out=None, acc=None, stream=None):
         import torch
