@@ -450,6 +450,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="c1")
+    ap.add_argument("--ctx", type=int, default=0, help="cached positions per sequence (default: the configuration's)")
     ap.add_argument("--batches", default=None,
                     help="first is the headline; others are reported alongside (default: 1,8; 1 for the verify "
                          "configuration c2; 8 for c3)")
@@ -485,6 +486,10 @@ def main() -> int:
         log(f"calibration copy: {args.calib_copy} MiB read, {args.calib_copy} MiB written")
         del src, dst
     cfg = synth.CONFIGS[args.config]
+    if args.ctx:
+        from dataclasses import replace
+
+        cfg = replace(cfg, ctx=args.ctx)
     m = build_gpu(cfg, max(batches))
     if args.plain_launch:
         m.set_launch_mode(False)
@@ -530,7 +535,7 @@ def main() -> int:
         log(f"plain read reference (float32 row sums over 8 GiB): {stream:.0f} GB/s "
             f"({100 * stream / accounting.HBM_PEAK_GBS:.1f}% of 8 TB/s)")
     cpu = None
-    if not args.no_cpu and cfg.name == "c1":
+    if not args.no_cpu and cfg.name == "c1" and not args.ctx:
         try:
             cpu = cpu_baseline(cfg)
             log(f"cpu oracle: {cpu['value']:.4f} tok/s on {cpu['cores']} threads ({cpu['sample']})")
