@@ -476,7 +476,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    default_batches = {"c0": "1", "c1": "1,2,4,8", "c2": "1", "c3": "8", "c4": "1,4,8"}
+    default_batches = {"c0": "1", "c1": "1,2,4,8,16", "c2": "1", "c3": "8", "c4": "1,4,8"}
     batches = [int(b) for b in (args.batches or default_batches.get(args.config, "1,8")).split(",")]
     if args.calib_copy:
         src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")

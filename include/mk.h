@@ -38,7 +38,10 @@ extern "C" {
 #endif
 
 #define MK_MAX_LAYERS 128
-#define MK_MAX_BATCH 8
+/* Rows of a decode step. Each activation enters the matrix products as a bf16 high and a bf16 low half
+ * (16 significant bits): one matrix-core product per weight fragment covers 8 rows, two cover 9 to 16.
+ * Mixture-of-experts configurations run at most 8 rows. */
+#define MK_MAX_BATCH 16
 #define MK_VERIFY_ROWS 8
 
 typedef enum {

@@ -1,7 +1,7 @@
 """Build step for the HIP library (libmk.so, gfx950) and the host-side input generator.
 
-Compiles in-tree with hipcc so the built library travels with the source tree. The library has three
-translation units (the host runtime and the two builds of the step kernel), compiled in parallel and
+Compiles in-tree with hipcc so the built library travels with the source tree. The library has four
+translation units (the host runtime and the three builds of the step kernel), compiled in parallel and
 linked together. Every HIP translation unit is built with packed fp32 instructions disabled (they are
 emitted only from ordinary float code otherwise, and some of their forms are not trusted on this
 hardware)."""
@@ -21,7 +21,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
-UNITS = ["mk_host.cpp", "mk_step.hip", "mk_step_nvfp4.hip"]
+UNITS = ["mk_host.cpp", "mk_step.hip", "mk_step_nvfp4.hip", "mk_step_wide.hip"]
 
 
 def build_lib(verbose: bool = False, extra_flags=()) -> str:

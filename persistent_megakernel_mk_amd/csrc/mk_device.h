@@ -88,7 +88,7 @@ __device__ __forceinline__ float *part_of(CArgs &a, int i) {
 __device__ __forceinline__ int pos_of(CArgs &a, int i) {
   int p = a.pos[0];
 #pragma unroll
-  for (int k = 1; k < kMaxRows; ++k)
+  for (int k = 1; k < kMaxBatch; ++k)
     if (i == k) p = a.pos[k];
   return p;
 }
@@ -191,13 +191,15 @@ struct RouteLds {
 constexpr int kRedSlots = 8;  // unit partials in flight between the compute waves and the sync wave
 struct GemvLds {
   static constexpr int act = 0;                                                 // kActLdsBudget bytes
-  static constexpr int red = kActLdsBudget;                                     // [kRedSlots][kCWaves][16][kMaxRows] f32
-  static constexpr int flags = red + kRedSlots * kCWaves * 16 * kMaxRows * 4;   // posted[kRedSlots], consumed[kRedSlots]
+  static constexpr int red = kActLdsBudget;                                     // [kRedSlots][kCWaves][16][kMaxBatch] f32
+  static constexpr int flags = red + kRedSlots * kCWaves * 16 * kMaxBatch * 4;  // posted[kRedSlots], consumed[kRedSlots]
   static constexpr int misc = flags + 2 * kRedSlots * 4;                        // rstd, finalizer flags, candidates
   static constexpr int route = misc + 8192;                                     // RouteLds
   static constexpr int end = route + (int)sizeof(RouteLds);
 };
 static_assert(GemvLds::end <= kLdsBytes, "product-phase LDS layout exceeds the workgroup's LDS");
+static_assert((16 + kMaxUnits + 512 + 16 * kMaxBatch) * 4 <= GemvLds::route - GemvLds::misc,
+              "product-phase scratch (1/rms, unit flags, argmax candidates, tile sums) exceeds its LDS region");
 
 __device__ __forceinline__ const RouteLds *route_lds(const char *smem) {
   return reinterpret_cast<const RouteLds *>(smem + GemvLds::route);
@@ -333,6 +335,11 @@ struct Stream {
 
 __device__ __forceinline__ int items_per_frag_row(const Phase &ph) { return ph.fmt == FMT_NVFP4 ? ph.KF / 4 : ph.KF; }
 
+// The compute waves' shares of the n items of a k-split: contiguous runs, the first n % 4 waves one
+// item longer (the schedule makes n a multiple of 4 up to kMaxRows rows; above, any n >= 4).
+__device__ __forceinline__ int wave_items(int n, int w) { return n / kCWaves + (w < n % kCWaves ? 1 : 0); }
+__device__ __forceinline__ int wave_first(int n, int w) { return w * (n / kCWaves) + min(w, n % kCWaves); }
+
 // first item of segment seg, tile t (its own weight block for expert phases), this wave's run
 __device__ __forceinline__ void stream_at(Stream &st, CArgs &a, CPhase *ph, const char *smem, int s, int seg,
                                           int t, int wave) {
@@ -342,7 +349,7 @@ __device__ __forceinline__ void stream_at(Stream &st, CArgs &a, CPhase *ph, cons
   int64_t tile = t;
   if (ph->seg == SEG_EXPERT) base += (int64_t)__builtin_amdgcn_readfirstlane(route_lds(smem)->expert[seg]) * ph->seg_stride;
   else tile += (int64_t)seg * ph->seg_T;
-  const int64_t item = tile * KI + s * nfi + wave * st.nfw;
+  const int64_t item = tile * KI + s * nfi + wave_first(nfi, wave);
   st.ptr = reinterpret_cast<const uint4 *>(base) + item * 64;
   if (ph->fmt == FMT_NVFP4) {
     const int Tm = ph->seg == SEG_EXPERT ? ph->seg_T : ph->T;
@@ -371,7 +378,7 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
         const bool fp4 = ph->fmt == FMT_NVFP4;
         const int nfi = fp4 ? ph->nf / 4 : ph->nf;
         st.q = q;
-        st.nfw = nfi / kCWaves;
+        st.nfw = wave_items(nfi, wave);
         st.left = u1 - u0;
         st.j = 0;
         st.skip = (fp4 ? ph->KF / 4 : ph->KF) - st.nfw;
@@ -468,12 +475,19 @@ __device__ __forceinline__ void lds_wait_ge(uint32_t *p, uint32_t v, CArgs &a) {
 // activation; one for all (the RMSNorm input of expert gate/up products and of unsegmented products).
 __device__ __forceinline__ bool shared_act(const Phase &ph) { return ph.seg == SEG_NONE || ph.act == ACT_NORM; }
 __device__ __forceinline__ int first_piece_seg(const Phase &ph, int u0) { return shared_act(ph) ? 0 : u0 / ph.seg_T; }
+// B-operand layout of the activation fragments: per group of up to 8 rows, 16 columns holding the group's
+// bf16 high halves, then its low halves. One group (2R columns) up to kMaxRows rows; above, two groups
+// (rows 0..7 and 8..R-1) of 16 columns each, multiplied by two MFMAs per weight fragment.
+template <bool WIDE>
+__device__ __forceinline__ int act_stride(int R) { return WIDE ? 32 : 2 * R; }
 
 // Stages the activation fragments of k-split s in LDS: for each piece (segment), row b and column k
 // the fp32 value y, split into a bf16 high part and a bf16 low part (y - high), laid out as the B
-// operand of v_mfma_f32_16x16x32_bf16 (columns 0..R-1 high parts, R..2R-1 low parts). For an RMSNorm
+// operand of v_mfma_f32_16x16x32_bf16 (per row group of Rg rows: columns 0..Rg-1 high parts,
+// Rg..2Rg-1 low parts). For an RMSNorm
 // input, y is x * gain: the per-row factor 1/rms is applied to the product's outputs (the product is
 // linear). Expert down products scale each row's activation by its routing weight.
+template <bool WIDE>
 __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u0, int u1, char *smem) {
   const int R = a.R;
   const int nk = ph.nf * kFragK;
@@ -534,10 +548,11 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
       hi[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
       lo[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
-    const int f = kg >> 2, g4 = kg & 3;
-    uint4 *pa = act + (size_t)pc * (nk / 8) * (2 * R);
-    pa[(f * 4 + g4) * (2 * R) + b] = uint4{hi[0], hi[1], hi[2], hi[3]};
-    pa[(f * 4 + g4) * (2 * R) + R + b] = uint4{lo[0], lo[1], lo[2], lo[3]};
+    const int f = kg >> 2, g4 = kg & 3, C = act_stride<WIDE>(R);
+    const int grp = WIDE ? b >> 3 : 0, bl = WIDE ? b & 7 : b, Rg = WIDE ? min(8, R - 8 * grp) : R;
+    uint4 *pa = act + (size_t)pc * (nk / 8) * C + grp * 16;
+    pa[(f * 4 + g4) * C + bl] = uint4{hi[0], hi[1], hi[2], hi[3]};
+    pa[(f * 4 + g4) * C + Rg + bl] = uint4{lo[0], lo[1], lo[2], lo[3]};
   }
 }
 
@@ -547,53 +562,55 @@ __device__ __forceinline__ bool needs_finalise(const Phase &ph) {
 }
 
 // Finalisation of one tile by the sync wave: every lane sums its (row, b) values of the tile over the
-// partials in partial order (plus the residual), with the loads of sixteen partials in flight at a time
+// partials in partial order (plus the residual), with the loads of 16 (8 above 8 rows) partials in flight at a time
 // (an expert down product has one partial per (expert, k-split), so a tile can have over a hundred);
 // device-coherent loads read the other contributors' partials (no cache invalidation). Stores the
 // residual and the tile's sums of squares, or the logits and the argmax candidate of each row (kept by
 // lane b).
+template <int NK>  // 64-lane groups of (row, b) values: 16 R / 64, so 2 up to 8 rows, 4 up to 16
 __device__ __forceinline__ void finalise_tiles(CArgs &a, const Phase &ph, int tile, int S_eff, int TN, float &best_v,
                                                int &best_i) {
-  constexpr int kFinBatch = 16;
+  constexpr int kFinBatch = 32 / NK;  // partial loads in flight per lane group: 16 up to 8 rows, 8 above
   const int R = a.R, lane = threadIdx.x & 63;
   const float *pp = part_of(a, ph.dst_part);
   const size_t pstride = (size_t)R * TN;
   const bool resid = ph.out == OUT_RESID;
-  int row_k[2], b_k[2];
-  bool ok_k[2];
-  size_t off[2];  // element offsets within a partial (a valid dummy for lanes without a value)
+  int row_k[NK], b_k[NK];
+  bool ok_k[NK];
+  size_t off[NK];  // element offsets within a partial (a valid dummy for lanes without a value)
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < NK; ++k) {
     const int idx = lane + 64 * k;
     ok_k[k] = idx < 16 * R;
     b_k[k] = ok_k[k] ? idx >> 4 : 0;  // lanes 16 b .. 16 b + 15: the tile's 16 rows of row b
     row_k[k] = idx & 15;
     off[k] = ok_k[k] ? (size_t)b_k[k] * TN + tile * kTileRows + row_k[k] : 0;
   }
-  float kb_v[2] = {-INFINITY, -INFINITY};  // logits: best of this lane's (row b_k) values
-  int kb_i[2] = {0x7fffffff, 0x7fffffff};
-  float acc[2] = {0.0f, 0.0f};
+  float kb_v[NK], acc[NK];  // logits: best of this lane's (row b_k) values; the sums
+  int kb_i[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) { kb_v[k] = -INFINITY; kb_i[k] = 0x7fffffff; acc[k] = 0.0f; }
   for (int s0 = 0; s0 < S_eff; s0 += kFinBatch) {
-    float t[kFinBatch][2];
+    float t[kFinBatch][NK];
 #pragma unroll
     for (int j = 0; j < kFinBatch; ++j) {
       const float *ps = pp + (size_t)min(s0 + j, S_eff - 1) * pstride;  // in bounds past the last partial
 #pragma unroll
-      for (int k = 0; k < 2; ++k) t[j][k] = s0 + j < S_eff ? ld_c(ps + off[k]) : 0.0f;
+      for (int k = 0; k < NK; ++k) t[j][k] = s0 + j < S_eff ? ld_c(ps + off[k]) : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < kFinBatch; ++j)
       if (s0 + j < S_eff) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) acc[k] += t[j][k];
+        for (int k = 0; k < NK; ++k) acc[k] += t[j][k];
       }
   }
-  float xv[2];  // the residual values this tile updates (loaded together)
+  float xv[NK];  // the residual values this tile updates (loaded together)
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
+  for (int k = 0; k < NK; ++k)
     xv[k] = resid ? ld_c(a.x + (ok_k[k] ? (size_t)b_k[k] * a.H + tile * kTileRows + row_k[k] : 0)) : 0.0f;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < NK; ++k) {
     const int n = tile * kTileRows + row_k[k], b = b_k[k];
     float v = acc[k];
     if (resid) {
@@ -615,7 +632,7 @@ __device__ __forceinline__ void finalise_tiles(CArgs &a, const Phase &ph, int ti
       float bv = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int k = 0; k < NK; ++k)
         if (ok_k[k] && b_k[k] == b) { bv = kb_v[k]; bi = kb_i[k]; }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
@@ -645,43 +662,54 @@ __device__ __forceinline__ bf16x8 nvfp4_frag(uint32_t codes, float scale) {
 // compute waves: consume this phase's items from the ring, refilling each slot from the stream.
 // A finished 16-row unit is handed to the sync wave through an LDS slot and a counter, without a
 // workgroup barrier, so the four waves never wait for each other inside a phase.
-template <bool HAS_FP4, int D>
+template <bool HAS_FP4, int D, bool WIDE>
 __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, uint4 (&ring)[D], uint32_t (&sring)[D],
                                          Stream &st, int &head, int s, int u0, int u1) {
   const int R = a.R;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const bool FP4 = HAS_FP4 && ph.fmt == FMT_NVFP4;
-  const int nfw = ph.nf / kCWaves;                // fragments per unit run of this wave
+  const int nfw = wave_items(ph.nf, wave);        // fragments per unit run of this wave (NVFP4: a multiple of 4)
   const int ipr = FP4 ? nfw / 4 : nfw;            // ring items per unit run
   const int total = (u1 - u0) * ipr;
   float *red = reinterpret_cast<float *>(smem + GemvLds::red);
   uint32_t *posted = reinterpret_cast<uint32_t *>(smem + GemvLds::flags);
   uint32_t *consumed = posted + kRedSlots;
-  const int piece_u4 = ph.nf * 4 * (2 * R);       // uint4 per activation piece
+  const int C = act_stride<WIDE>(R);              // activation columns of the B operand (both groups)
+  const int R1 = WIDE ? R - 8 : 0;                // rows of the second group
+  const int piece_u4 = ph.nf * 4 * C;             // uint4 per activation piece
   const uint4 *actv = reinterpret_cast<const uint4 *>(smem + GemvLds::act);
   const bool per_seg = !shared_act(ph);
   const int j0 = first_piece_seg(ph, u0);
   int c_j = 0, unit = 0;
   int seg_left = per_seg ? ph.seg_T - (u0 - j0 * ph.seg_T) : 0x40000000;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};  // acc1: rows 8.. (WIDE)
   const int col = lane & 15, kgrp = lane >> 4;
-  const uint4 *aw = actv + (size_t)wave * nfw * 4 * (2 * R);
+  const uint4 *aw = actv + (size_t)wave_first(ph.nf, wave) * 4 * C;
   auto close_unit = [&]() {  // combine hi/lo columns and post this wave's 16 x R partials
-    float v[4];
+    float v[4], v1[4];
+    const int R0 = WIDE ? 8 : R;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = acc[e] + __shfl_down(acc[e], R);
+    for (int e = 0; e < 4; ++e) {
+      v[e] = acc[e] + __shfl_down(acc[e], R0);
+      v1[e] = WIDE ? acc1[e] + __shfl_down(acc1[e], R1) : 0.0f;
+    }
     const int sl = unit % kRedSlots;
     const uint32_t use = (uint32_t)(unit / kRedSlots);
     if (lds_ld(consumed + sl) < use) lds_wait_ge(consumed + sl, use, a);  // slot free (the sync wave read it)
-    float *rb = red + (sl * kCWaves + wave) * 16 * kMaxRows;
-    if (col < R) {
+    float *rb = red + (sl * kCWaves + wave) * 16 * kMaxBatch;
+    if (col < R0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rb[(kgrp * 4 + e) * kMaxRows + col] = v[e];
+      for (int e = 0; e < 4; ++e) rb[(kgrp * 4 + e) * kMaxBatch + col] = v[e];
+    }
+    if (WIDE && col < R1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rb[(kgrp * 4 + e) * kMaxBatch + 8 + col] = v1[e];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_fetch_add(posted + sl, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     ++unit;
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
     c_j = 0;
     if (--seg_left == 0) {  // next segment: its own activation piece
       aw += piece_u4;
@@ -697,15 +725,21 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         uint4 bv = uint4{0u, 0u, 0u, 0u};
-        if (col < 2 * R) bv = aw[((c_j * 4 + f) * 4 + kgrp) * (2 * R) + col];
+        if (col < 2 * R) bv = aw[((c_j * 4 + f) * 4 + kgrp) * C + col];
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nvfp4_frag(cw[f], sc4[f]), __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);  // one fragment's dequantised weights live at a time
       }
     } else {
       uint4 bv = uint4{0u, 0u, 0u, 0u};
-      if (col < 2 * R) bv = aw[(c_j * 4 + kgrp) * (2 * R) + col];
+      if (col < (WIDE ? 16 : 2 * R)) bv = aw[(c_j * 4 + kgrp) * C + col];
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r), __builtin_bit_cast(bf16x8, bv), acc, 0,
                                                     0, 0);
+      if (WIDE) {  // the second row group: the same weight fragment against its 16 columns
+        uint4 bv1 = uint4{0u, 0u, 0u, 0u};
+        if (col < 2 * R1) bv1 = aw[(c_j * 4 + kgrp) * C + 16 + col];
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r), __builtin_bit_cast(bf16x8, bv1), acc1,
+                                                       0, 0, 0);
+      }
     }
     stream_take(st, a, smem, wave, lane, r, sc);  // the slot's old item is consumed: refill it
     if (++c_j == ipr) close_unit();
@@ -724,7 +758,7 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
   head = rem;
 }
 
-template <bool HAS_FP4, int D>
+template <bool HAS_FP4, int D, bool WIDE>
 __device__ __forceinline__ void gemv_compute(CArgs &a, const Phase &ph, char *smem, uint4 (&ring)[D], uint32_t (&sring)[D],
                                              Stream &st, int &head) {
   int s, u0, u1;
@@ -734,13 +768,14 @@ __device__ __forceinline__ void gemv_compute(CArgs &a, const Phase &ph, char *sm
     ring_rotate(sring, head);
     head = 0;
   }
-  if (u1 > u0) prep_act(a, ph, s, u0, u1, smem);
+  if (u1 > u0) prep_act<WIDE>(a, ph, s, u0, u1, smem);
   lds_barrier();  // activation fragments ready, handoff counters cleared
-  gemv_run<HAS_FP4>(a, ph, smem, ring, sring, st, head, s, u0, u1);
+  gemv_run<HAS_FP4, D, WIDE>(a, ph, smem, ring, sring, st, head, s, u0, u1);
 }
 
 // sync wave: activation staging (with the compute waves), norm statistics, per-unit reduction and
 // stores, finalisation
+template <bool WIDE>
 __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, lane = threadIdx.x & 63;
   int s, u0, u1;
@@ -750,10 +785,10 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   uint32_t *posted = reinterpret_cast<uint32_t *>(smem + GemvLds::flags);
   uint32_t *consumed = posted + kRedSlots;
   float *misc = reinterpret_cast<float *>(smem + GemvLds::misc);
-  float *rstd = misc;                                        // [kMaxRows]
+  float *rstd = misc;                                        // [kMaxBatch]
   int *flags = reinterpret_cast<int *>(misc + 16);           // [kMaxUnits]
-  float *cval = misc + 16 + kMaxUnits;                       // [128]
-  int *cidx = reinterpret_cast<int *>(cval + 128);           // [128]
+  float *cval = misc + 16 + kMaxUnits;                       // [256]
+  int *cidx = reinterpret_cast<int *>(cval + 256);           // [256]
   const RouteLds *rt = route_lds(smem);
   const bool direct = ph.out == OUT_LOGITS && ph.S == 1;
   const bool expert = ph.seg == SEG_EXPERT;
@@ -762,7 +797,7 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   const int S_eff = expert ? rt->nseg * ph.S : ph.S;
   const int TN = expert ? ph.seg_T * kTileRows : ph.N;  // rows of the finalised output
   if (lane < 2 * kRedSlots) posted[lane] = 0u;  // posted[] and consumed[] (adjacent)
-  if (nunits > 0) prep_act(a, ph, s, u0, u1, smem);
+  if (nunits > 0) prep_act<WIDE>(a, ph, s, u0, u1, smem);
   lds_barrier();  // activation fragments ready, handoff counters cleared
   if (ph.act == ACT_NORM) {  // 1/rms of each row from the per-tile sums of squares (while the waves stream)
     const int nt = a.H / kTileRows;
@@ -774,12 +809,16 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     }
     wave_lds_sync();
   }
-  float rs[2] = {1.0f, 1.0f};
+  // lane groups k hold (row = idx / R, b = idx % R) for idx = lane + 64 k < 16 R: 2 groups up to 8 rows, 4 up to 16
+  constexpr int NK = WIDE ? 4 : 2;
+  float rs[NK], best_v[NK];
+  int best_i[NK];
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
-    if (ph.act == ACT_NORM && lane + 64 * k < 16 * R) rs[k] = rstd[(lane + 64 * k) % R];
-  float best_v[2] = {-INFINITY, -INFINITY};
-  int best_i[2] = {0x7fffffff, 0x7fffffff};
+  for (int k = 0; k < NK; ++k) {
+    rs[k] = (ph.act == ACT_NORM && lane + 64 * k < 16 * R) ? rstd[(lane + 64 * k) % R] : 1.0f;
+    best_v[k] = -INFINITY;
+    best_i[k] = 0x7fffffff;
+  }
   const float *ts = reinterpret_cast<const float *>(a.wbuf + ph.ts_off);
   const int nrot = u1 - u0, r0 = rotated(ph) ? rot_start(s, ph.S, nrot) : 0;
   const bool fin = needs_finalise(ph);
@@ -800,16 +839,17 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     }
     if (lds_ld(posted + sl) < need) lds_wait_ge(posted + sl, need, a);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    const float *rb = red + sl * kCWaves * 16 * kMaxRows;
-    float xsq[2] = {0.0f, 0.0f};
+    const float *rb = red + sl * kCWaves * 16 * kMaxBatch;
+    float xsq[NK];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NK; ++k) {
+      xsq[k] = 0.0f;
       const int idx = lane + 64 * k;
       if (idx < 16 * R) {
         const int row = idx / R, b = idx % R;
         float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kCWaves; ++w) v += rb[(w * 16 + row) * kMaxRows + b];
+        for (int w = 0; w < kCWaves; ++w) v += rb[(w * 16 + row) * kMaxBatch + b];
         v *= rs[k] * sc;
         if (direct) {
           const int n = u * kTileRows + row;
@@ -830,9 +870,9 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_store(consumed + sl, (uint32_t)(unit / kRedSlots + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (direct_resid) {  // the tile's sum of squares per row: lanes hold (row = idx / R, b = idx % R)
-      float *sqs = misc + 16 + kMaxUnits + 256;  // [16][kMaxRows]
+      float *sqs = misc + 16 + kMaxUnits + 512;  // [16][kMaxBatch]
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int k = 0; k < NK; ++k)
         if (lane + 64 * k < 16 * R) sqs[lane + 64 * k] = xsq[k];
       wave_lds_sync();
       if (lane < R) {
@@ -853,12 +893,12 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
         last = old + 1u == (uint32_t)S_eff;
         if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (__shfl(last, 0)) finalise_tiles(a, ph, tl, S_eff, TN, best_v[0], best_i[0]);
+      if (__shfl(last, 0)) finalise_tiles<NK>(a, ph, tl, S_eff, TN, best_v[0], best_i[0]);
     }
   }
   if (ph.out == OUT_LOGITS) {  // per-workgroup argmax candidate of each row (first index on ties)
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NK; ++k) {
       cval[lane + 64 * k] = best_v[k];
       cidx[lane + 64 * k] = best_i[k];
     }
@@ -1531,9 +1571,9 @@ __device__ __forceinline__ void embed_phase(CArgs &a, const Phase &ph, char *sme
 __device__ __forceinline__ void final_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, G = gridDim.x, tid = threadIdx.x;
   float *cv = reinterpret_cast<float *>(smem);
-  int *ci = reinterpret_cast<int *>(cv + G * kMaxRows);
-  int *am = ci + G * kMaxRows;
-  int *acc_s = am + kMaxRows;
+  int *ci = reinterpret_cast<int *>(cv + G * kMaxBatch);
+  int *am = ci + G * kMaxBatch;
+  int *acc_s = am + kMaxBatch;
   if (a.V > 0) {
     for (int idx = tid; idx < G * R; idx += kThreads) {
       cv[idx] = ld_c(a.cand + (size_t)idx * 2);
@@ -1616,7 +1656,7 @@ __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *sm
 // stores cross-workgroup results and runs the grid barrier. The two kinds of wave run separate copies
 // of the phase loop with the same sequence of workgroup barriers, so the weight ring is not live in
 // the sync wave's code.
-template <bool HAS_FP4, int RING>
+template <bool HAS_FP4, int RING, bool WIDE = false>
 __device__ __forceinline__ void step_body(char *smem) {
   CArgs *ap = (CArgs *)__builtin_amdgcn_kernarg_segment_ptr();
   __shared__ int abort_flag;
@@ -1633,7 +1673,7 @@ __device__ __forceinline__ void step_body(char *smem) {
           compute_route(a, ph, smem);
           route_q = ph.route_q;
         }
-        gemv_sync(a, ph, smem);
+        gemv_sync<WIDE>(a, ph, smem);
       } else {
         common_phase(a, ph, smem);
       }
@@ -1677,7 +1717,7 @@ __device__ __forceinline__ void step_body(char *smem) {
           for (int d = 0; d < RING; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
           head = 0;
         }
-        gemv_compute<HAS_FP4, RING>(a, ph, smem, ring, sring, st, head);
+        gemv_compute<HAS_FP4, RING, WIDE>(a, ph, smem, ring, sring, st, head);
       } else {
         common_phase(a, ph, smem);
       }

@@ -25,6 +25,7 @@ using namespace mk;
 
 extern "C" __global__ void mk_step_kernel(StepArgs a);
 extern "C" __global__ void mk_step_kernel_nvfp4(StepArgs a);
+extern "C" __global__ void mk_step_kernel_wide(StepArgs a);
 extern "C" __global__ void mk_repack_bf16(const uint16_t *src, int64_t rows, int64_t cols, uint4 *dst, int64_t row_off,
                                           int64_t KF);
 extern "C" __global__ void mk_repack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
@@ -128,11 +129,11 @@ struct mk_ctx {
   int n_lin = 0, n_resid = 0, n_moe = 0, max_rows = 1;
   std::vector<int> lin_index;  // per layer: index among linear-attention layers (-1 otherwise)
   int mix_stride = 0;
-  Schedule sched[kMaxRows + 1];  // by row count
+  Schedule sched[kMaxBatch + 1];  // by row count
   // scratch layout (byte offsets)
   int64_t o_rope_mla = 0, o_loop = 0;
   int64_t o_status = 0, o_bar = 0, o_fin = 0, o_x = 0, o_ss = 0, o_part[3] = {0, 0, 0}, o_mix = 0, o_attn = 0,
-          o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxRows + 1] = {}, scratch_bytes = 0;
+          o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxBatch + 1] = {}, scratch_bytes = 0;
   int64_t kv_bytes = 0, lin_bytes = 0, latent_bytes = 0;
   // bound buffers
   bool bound = false;
@@ -148,8 +149,8 @@ struct mk_ctx {
   bool nvfp4 = false;         // the schedule has NVFP4 products: the step kernel build that decodes them
   // per-op baseline graphs: one instantiated graph per row count, with the launch arguments it was
   // captured with (a call whose arguments differ captures again), and the stream it is captured on
-  hipGraphExec_t graph[kMaxRows + 1] = {};
-  StepArgs graph_args[kMaxRows + 1];
+  hipGraphExec_t graph[kMaxBatch + 1] = {};
+  StepArgs graph_args[kMaxBatch + 1];
   hipStream_t capture_stream = nullptr;
 };
 
@@ -178,6 +179,7 @@ mk_status validate(const mk_config *c) {
   }
   if (any_dense && (c->ffn <= 0 || c->ffn % 256)) return fail(MK_E_UNSUPPORTED, "ffn %d must be a positive multiple of 256", c->ffn);
   if (any_moe) {
+    if (c->max_batch > kMaxRows) return fail(MK_E_UNSUPPORTED, "mixture-of-experts layers run at most %d rows per step", kMaxRows);
     if (c->n_experts < 1 || c->n_experts > kMaxExperts) return fail(MK_E_UNSUPPORTED, "n_experts %d out of [1, %d]", c->n_experts, kMaxExperts);
     if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_experts)
       return fail(MK_E_UNSUPPORTED, "top_k %d out of [1, min(%d, n_experts)]", c->top_k, kMaxTopK);
@@ -217,7 +219,8 @@ mk_status validate(const mk_config *c) {
 
 // Chooses the k-split count of a product: a power of two dividing the workgroup count (each
 // workgroup works inside one split), nf = KF / S a multiple of the compute-wave count (of four times
-// it for NVFP4, whose stream items hold four fragments), the activation pieces of one workgroup within
+// it for NVFP4, whose stream items hold four fragments; above kMaxRows rows a bf16 split only needs a
+// fragment per wave, the waves taking runs one fragment apart), the activation pieces of one workgroup within
 // the LDS budget, and the fewest fragment-slots on the busiest workgroup (plus about one fragment's
 // time per unit for the cross-wave reduction). A product of nseg segments of segT tiles each gives every
 // segment its own activation when per_seg_act (one piece per segment a workgroup's units touch).
@@ -227,20 +230,22 @@ int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_
   double best_cost = 1e300;
   const int64_t U = (int64_t)segT * nseg;
   const int q = fp4 ? 4 * kCWaves : kCWaves;
+  const bool uneven = !fp4 && R > kMaxRows;
   for (int S = 1; S <= KF / q && S <= G; S *= 2) {
-    if (KF % S || (KF / S) % q || S > max_S || G % S) continue;
+    if (KF % S || (!uneven && (KF / S) % q) || S > max_S || G % S) continue;
     const int nf = KF / S;
     const int64_t per_split = G / S;                     // workgroups per k-split
     const int64_t per = (U + per_split - 1) / per_split; // units on the busiest workgroup
     if (per > kMaxUnits) continue;
     const int np = per_seg_act ? (int)std::min<int64_t>((per - 1 + segT - 1) / segT + 1, nseg) : 1;
     if (np > kMaxPieces) continue;
-    if ((int64_t)np * nf * 128 * R > kActLdsBudget) continue;
+    const int C = R <= kMaxRows ? 2 * R : 32;  // B-operand columns: bf16 high and low halves, 16 per group of 8 rows
+    if ((int64_t)np * nf * 64 * C > (R <= kMaxRows ? kActLdsBudgetNarrow : kActLdsBudget)) continue;
     // a residual product split over k also pays, per unit, the acknowledgement of its partials and the
     // tile counter round trip (about ten fragment times); with one split the unit adds into the
     // residual directly
     const double fin = (resid && S > 1) ? 10.0 * per : 0.0;
-    const double cost = (double)per * (nf / kCWaves + 1.0) + fin + 0.01 * S;
+    const double cost = (double)per * ((nf + kCWaves - 1) / kCWaves + 1.0) + fin + 0.01 * S;
     if (cost < best_cost) { best_cost = cost; best = S; best_pieces = np; }
   }
   if (pieces_out) *pieces_out = best_pieces;
@@ -609,7 +614,7 @@ mk_status scratch_layout(mk_ctx *c) {
     return o;
   };
   int64_t part[3] = {0, 0, 0}, attn = 0;
-  for (int r = 1; r <= kMaxRows; ++r) {
+  for (int r = 1; r <= kMaxBatch; ++r) {
     const Schedule &s = c->sched[r];
     if (s.phases.empty()) continue;
     for (int i = 0; i < 3; ++i) part[i] = std::max<int64_t>(part[i], s.part_floats[i]);
@@ -629,10 +634,10 @@ mk_status scratch_layout(mk_ctx *c) {
   c->o_snap = take(f.vocab > 0 ? (int64_t)c->n_lin * kMaxRows * f.lin_heads * f.d_v * f.d_k * 4 : 0);
   c->o_rope_mla = take(f.mla_heads > 0 ? (int64_t)f.max_ctx * (f.rope_dim / 2) * 2 * 4 : 0);
   c->o_ptrs = take((int64_t)5 * MK_MAX_LAYERS * 8);
-  for (int r = 1; r <= kMaxRows; ++r)
+  for (int r = 1; r <= kMaxBatch; ++r)
     if (!c->sched[r].phases.empty()) c->o_phases[r] = take((int64_t)c->sched[r].phases.size() * sizeof(Phase));
   int64_t max_phases = 0;
-  for (int r = 1; r <= kMaxRows; ++r) max_phases = std::max<int64_t>(max_phases, (int64_t)c->sched[r].phases.size());
+  for (int r = 1; r <= kMaxBatch; ++r) max_phases = std::max<int64_t>(max_phases, (int64_t)c->sched[r].phases.size());
   c->o_loop = take(f.vocab > 0 ? (int64_t)MK_MAX_LOOP_STEPS * max_phases * sizeof(Phase) : 0);  // multi-step tables
   c->scratch_bytes = off;
   c->kv_bytes = (int64_t)f.max_batch * f.n_kv_heads * f.max_ctx * f.head_dim * 2;
@@ -851,16 +856,19 @@ mk_status reset_counters(mk_ctx *c, hipStream_t st) {
   return MK_OK;
 }
 
-const void *step_kernel(const mk_ctx *c) {
-  return c->nvfp4 ? reinterpret_cast<const void *>(mk_step_kernel_nvfp4) : reinterpret_cast<const void *>(mk_step_kernel);
+// The step kernel build for a step of R rows: NVFP4 experts (at most 8 rows), bf16 up to 8 rows, or
+// bf16 above 8 rows (two row groups per weight fragment).
+const void *step_kernel(const mk_ctx *c, int R) {
+  if (c->nvfp4) return reinterpret_cast<const void *>(mk_step_kernel_nvfp4);
+  return R > kMaxRows ? reinterpret_cast<const void *>(mk_step_kernel_wide) : reinterpret_cast<const void *>(mk_step_kernel);
 }
 
 mk_status launch_step(mk_ctx *c, StepArgs &a, hipStream_t st) {
   void *args[] = {&a};
   if (c->cooperative) {
-    HIP_TRY(hipLaunchCooperativeKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
+    HIP_TRY(hipLaunchCooperativeKernel(step_kernel(c, a.R), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
   } else {
-    HIP_TRY(hipLaunchKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
+    HIP_TRY(hipLaunchKernel(step_kernel(c, a.R), dim3(c->G), dim3(kThreads), args, kLdsBytes, st));
   }
   return MK_OK;
 }
@@ -946,7 +954,7 @@ mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
   mk_ctx *c = new mk_ctx();
   c->cfg = *cfg;
   c->device = hip_device;
-  c->max_rows = cfg->vocab > 0 ? kMaxRows : cfg->max_batch;
+  c->max_rows = cfg->vocab > 0 ? std::max(kMaxRows, cfg->max_batch) : cfg->max_batch;  // verify blocks have kMaxRows rows
   for (int l = 0; l < cfg->n_layers; ++l)
     if (cfg->ffn_kind[l] == MK_FFN_MOE && cfg->expert_format == MK_DT_NVFP4) c->nvfp4 = true;
   if (hip_device >= 0) {
@@ -963,7 +971,7 @@ mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
   }
   memset(&c->bufs, 0, sizeof(c->bufs));
   mk_status st = layout(c);
-  for (int r = 1; st == MK_OK && r <= kMaxRows; ++r) {
+  for (int r = 1; st == MK_OK && r <= kMaxBatch; ++r) {
     if (r > c->max_rows) break;
     st = build_schedule(c, r, c->sched[r]);
   }
@@ -971,14 +979,16 @@ mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
   if (st != MK_OK) { delete c; return st; }
   if (hip_device >= 0) {
     hipError_t e = hipSetDevice(hip_device);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(step_kernel(c), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) { delete c; return fail(MK_E_HIP, "kernel setup: %s", hipGetErrorString(e)); }
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, step_kernel(c), kThreads, kLdsBytes);
-    if (e != hipSuccess || nb < 1) {
-      delete c;
-      return fail(MK_E_HIP, "step kernel cannot be resident (%d per CU): %s", nb, hipGetErrorString(e));
+    for (int R : {1, c->max_rows}) {  // the builds this context launches
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(step_kernel(c, R), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      if (e != hipSuccess) { delete c; return fail(MK_E_HIP, "kernel setup: %s", hipGetErrorString(e)); }
+      int nb = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, step_kernel(c, R), kThreads, kLdsBytes);
+      if (e != hipSuccess || nb < 1) {
+        delete c;
+        return fail(MK_E_HIP, "step kernel cannot be resident (%d per CU): %s", nb, hipGetErrorString(e));
+      }
     }
     if (mk_status s = noalloc_init(hip_device)) { delete c; return s; }
   }
@@ -1052,7 +1062,7 @@ mk_status mk_bind_buffers(mk_ctx *c, const mk_buffers *b) {
       }
     HIP_TRY(hipMemcpy(c->scratch + c->o_rope_mla, rope.data(), rope.size() * 4, hipMemcpyHostToDevice));
   }
-  for (int r = 1; r <= kMaxRows; ++r) {
+  for (int r = 1; r <= kMaxBatch; ++r) {
     const Schedule &s = c->sched[r];
     if (s.phases.empty()) continue;
     HIP_TRY(hipMemcpy(c->scratch + c->o_phases[r], s.phases.data(), s.phases.size() * sizeof(Phase), hipMemcpyHostToDevice));
@@ -1255,7 +1265,7 @@ mk_status mk_decode_step_perop(mk_ctx *c, const mk_step_io *io, int batch, int u
       ap.phase_end = p + 1;
       ap.barrier_base = p;
       void *args[] = {&ap};
-      HIP_TRY(hipLaunchKernel(step_kernel(c), dim3(c->G), dim3(kThreads), args, kLdsBytes, s));
+      HIP_TRY(hipLaunchKernel(step_kernel(c, ap.R), dim3(c->G), dim3(kThreads), args, kLdsBytes, s));
     }
     return MK_OK;
   };
@@ -1314,7 +1324,7 @@ mk_status mk_set_trace(mk_ctx *c, void *device_buffer, int64_t bytes) {
   if (!c) return fail(MK_E_ARG, "ctx is NULL");
   if (device_buffer) {
     int64_t need = 0;
-    for (int r = 1; r <= kMaxRows; ++r) need = std::max<int64_t>(need, (int64_t)c->sched[r].phases.size() * c->G * 16);
+    for (int r = 1; r <= kMaxBatch; ++r) need = std::max<int64_t>(need, (int64_t)c->sched[r].phases.size() * c->G * 16);
     if (bytes < need) return fail(MK_E_CAPACITY, "trace buffer %lld bytes < %lld", (long long)bytes, (long long)need);
     if ((uintptr_t)device_buffer & 7) return fail(MK_E_ARG, "trace buffer must be 8-byte aligned");
   }
@@ -1324,12 +1334,12 @@ mk_status mk_set_trace(mk_ctx *c, void *device_buffer, int64_t bytes) {
 
 // Host-logic introspection for tests (no device needed): the phase table for a row count.
 int mk_debug_phase_count(const mk_ctx *c, int rows) {
-  if (!c || rows < 1 || rows > kMaxRows) return -1;
+  if (!c || rows < 1 || rows > kMaxBatch) return -1;
   return (int)c->sched[rows].phases.size();
 }
 
 int mk_debug_phase(const mk_ctx *c, int rows, int i, int32_t *out16) {
-  if (!c || rows < 1 || rows > kMaxRows || i < 0 || i >= (int)c->sched[rows].phases.size() || !out16) return -1;
+  if (!c || rows < 1 || rows > kMaxBatch || i < 0 || i >= (int)c->sched[rows].phases.size() || !out16) return -1;
   const Phase &p = c->sched[rows].phases[(size_t)i];
   const int32_t v[16] = {p.type, p.layer, p.N, p.K, p.T, p.KF, p.S, p.nf, p.act, p.out, p.src_S, p.src_N, p.n_chunks, p.chunk,
                          p.dst_part, p.cnt_off};
@@ -1338,7 +1348,7 @@ int mk_debug_phase(const mk_ctx *c, int rows, int i, int32_t *out16) {
 }
 
 int mk_debug_phase_bytes(const mk_ctx *c, int rows, int i, void *out, int bytes) {
-  if (!c || rows < 1 || rows > kMaxRows || i < 0 || i >= (int)c->sched[rows].phases.size() || !out) return -1;
+  if (!c || rows < 1 || rows > kMaxBatch || i < 0 || i >= (int)c->sched[rows].phases.size() || !out) return -1;
   if (bytes < (int)sizeof(Phase)) return (int)sizeof(Phase);
   memcpy(out, &c->sched[rows].phases[(size_t)i], sizeof(Phase));
   return (int)sizeof(Phase);

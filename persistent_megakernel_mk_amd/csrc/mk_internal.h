@@ -12,11 +12,16 @@ constexpr int kThreads = kWavesTotal * 64;  // threads per workgroup
 constexpr int kCThreads = kCWaves * 64;     // threads of the compute waves
 constexpr int kRing = 12;                 // weight items in flight per compute wave (12 KiB), bf16 build
 constexpr int kRingNvfp4 = 10;            // the same for the build that also streams NVFP4 items
+constexpr int kRingWide = 10;             // the same for the build for more than 8 rows
 constexpr int kTileRows = 16;             // weight rows per MFMA tile
 constexpr int kFragK = 32;                // reduction columns per 1 KiB weight fragment
 constexpr int kLdsBytes = 160 * 1024 - 512;  // dynamic LDS per workgroup (gfx950: 160 KiB per CU, minus static)
-constexpr int kActLdsBudget = 96 * 1024;  // activation fragments of one k-split
-constexpr int kMaxRows = 8;               // rows per step (batch or verify block)
+constexpr int kActLdsBudget = 112 * 1024;     // LDS for the activation fragments of one k-split
+constexpr int kActLdsBudgetNarrow = 96 * 1024; // what the k-split choice uses up to kMaxRows rows
+constexpr int kMaxRows = 8;               // rows of a verify block; rows whose activations enter products
+                                          // as bf16 high and low halves (2 MFMA columns each)
+constexpr int kMaxBatch = 16;             // rows of a decode step; above kMaxRows each activation enters
+                                          // products as one bf16 column (the 16 columns hold 16 rows)
 constexpr int kMaxUnits = 512;            // product units (tile x k-split) per workgroup and phase
 constexpr int kMaxTopK = 16;              // routed experts per token
 constexpr int kMaxExperts = 1024;         // routed experts per MoE layer
@@ -134,7 +139,7 @@ struct StepArgs {
   // io
   const int32_t *tokens;
   const float *hidden_in;
-  int32_t pos[kMaxRows];  // position of each sequence's new token (verify: of the anchor)
+  int32_t pos[kMaxBatch];  // position of each sequence's new token (verify: of the anchor)
   float *logits;
   float *hidden_out;
   int32_t *argmax;

@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmk.so")
 
 MK_MAX_LAYERS = 128
-MK_MAX_BATCH = 8
+MK_MAX_BATCH = 16
 MK_VERIFY_ROWS = 8
 
 STATUS = {0: "MK_OK", 1: "MK_E_ARG", 2: "MK_E_SHAPE", 3: "MK_E_UNSUPPORTED", 4: "MK_E_CAPACITY", 5: "MK_E_HIP",
@@ -315,7 +315,7 @@ class Megakernel:
             io.route_w = route[1].data_ptr()
         io.tokens = tokens.data_ptr() if tokens is not None else None
         io.hidden_in = hidden_in.data_ptr() if hidden_in is not None else None
-        self._pos = (i32 * MK_VERIFY_ROWS)(*[int(p) for p in positions])
+        self._pos = (i32 * MK_MAX_BATCH)(*[int(p) for p in positions])
         io.positions = ctypes.cast(self._pos, vp)
         io.logits = logits.data_ptr() if logits is not None else None
         io.hidden_out = hidden_out.data_ptr() if hidden_out is not None else None

@@ -76,19 +76,21 @@ def make_gpu(cfg, W, S, max_batch=None, device=0):
     return m
 
 
-def compare_states(gpu_S, ref_S, new_positions=None):
+def compare_states(gpu_S, ref_S, new_positions=None, tol=None):
     """Caches: rows other than this step's new rows bit-identical; new rows (bf16 roundings of fp32
     projections that differ from the oracle's by summation order) within one bf16 ulp plus the
-    projection tolerance relative to the row's largest entry. Linear states: fp32, relative tolerance."""
+    projection tolerance relative to the row's largest entry. Linear states: fp32, relative tolerance.
+    tol replaces REL_TOL (steps whose activations enter products as bf16)."""
+    tol = REL_TOL if tol is None else tol
     for name, ref in ref_S.items():
         g = gpu_S[name]
         if name.endswith("lstate"):
             e = rel_err(g, ref)
-            assert e < REL_TOL, (name, e)
+            assert e < tol, (name, e)
             continue
         gf, rf = bf16_to_f32(g).astype(np.float64), bf16_to_f32(ref).astype(np.float64)
         rowmax = np.max(np.abs(rf), axis=-1, keepdims=True)
-        bound = np.maximum(np.abs(rf), np.abs(gf)) * 2.0 ** -7 + REL_TOL * rowmax
+        bound = np.maximum(np.abs(rf), np.abs(gf)) * 2.0 ** -7 + tol * rowmax
         diff = np.abs(gf - rf)
         assert np.all(diff <= bound), (name, float(diff.max()))
         if new_positions is not None:

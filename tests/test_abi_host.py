@@ -47,7 +47,11 @@ def test_invalid_configs_are_rejected(mkmod, synth):
             mkmod.HostContext(bad)
         assert ei.value.status == status
     with pytest.raises(mkmod.MKError):
-        mkmod.HostContext(cfg, max_batch=9)
+        mkmod.HostContext(cfg, max_batch=17)
+    mkmod.HostContext(cfg, max_batch=16)  # dense stacks take up to 16 rows
+    with pytest.raises(mkmod.MKError) as ei:  # mixture-of-experts layers at most 8
+        mkmod.HostContext(synth.CONFIGS["c4s"], max_batch=9)
+    assert ei.value.status == 3
 
 
 def test_schedule_layer_pattern_and_phase_counts(mkmod, synth):
@@ -68,16 +72,18 @@ def test_schedule_layer_pattern_and_phase_counts(mkmod, synth):
 
 def test_split_choice_respects_lds_and_waves(mkmod, synth):
     cfg = synth.CONFIGS["c1"]
-    h = mkmod.HostContext(cfg, max_batch=8)
-    for rows in range(1, 9):
+    h = mkmod.HostContext(cfg, max_batch=16)
+    for rows in range(1, 17):
+        cols = 2 * rows if rows <= 8 else 32  # bf16 high and low halves: 16 columns per group of 8 rows
         for p in h.phases(rows):
             if p[0] != 2:
                 continue
             N, K, T, KF, S, nf = p[2], p[3], p[4], p[5], p[6], p[7]
             assert T * 16 == N and KF * 32 == K
-            assert S >= 1 and KF == S * nf and nf % 4 == 0  # four streaming waves split a k-split
+            # four streaming waves split a k-split (evenly up to 8 rows; above, runs one fragment apart)
+            assert S >= 1 and KF == S * nf and (nf % 4 == 0 if rows <= 8 else nf >= 4)
             assert 256 % S == 0  # a power-of-two split count: each workgroup works inside one k-split
-            assert nf * 128 * rows <= 96 * 1024  # activation fragments of one split fit the LDS budget
+            assert nf * 64 * cols <= (96 if rows <= 8 else 112) * 1024  # activation fragments of one split fit
 
 
 def test_sizes(mkmod, synth):
