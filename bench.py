@@ -542,9 +542,11 @@ def main() -> int:
         except Exception as e:  # the CPU leg must not hide the GPU result
             log(f"cpu baseline failed: {e!r}")
     h = results[batches[0]]
+    # a verify step emits the accepted drafts plus the bonus token: (a + 1) tokens, not its 8 rows
+    value = (h["accepted"] + 1) / (h["mean_ms"] / 1e3) if h["accepted"] is not None else h["tokens_s"]
     line = {
         "metric": METRIC,
-        "value": round(h["tokens_s"], 3),
+        "value": round(value, 3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -577,7 +579,8 @@ def main() -> int:
         line["verify"] = {"drafts": "seeded: each draft the greedy continuation with probability 0.8, else a uniform "
                                     "other token", "tokens": [int(t) for t in drafts], "accepted": h["accepted"],
                           "emitted_per_step": h["accepted"] + 1,
-                          "emitted_tokens_s": round((h["accepted"] + 1) / (h["mean_ms"] / 1e3), 2)}
+                          "emitted_tokens_s": round((h["accepted"] + 1) / (h["mean_ms"] / 1e3), 2),
+                          "rows_s": round(h["tokens_s"], 2)}
     print(json.dumps(line), flush=True)
     return 0
 
