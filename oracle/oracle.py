@@ -78,6 +78,11 @@ def lib() -> ctypes.CDLL:
             "orc_silu_mul": ([vp, vp, i64, vp], None),
             "orc_argmax": ([vp, i64], i64),
             "orc_residual_add": ([vp, vp, i64], None),
+            "orc_e8m0_value": ([ctypes.c_uint8], f32),
+            "orc_mxfp4_dequant_row": ([vp, vp, i64, vp], None),
+            "orc_gemv_mxfp4": ([vp, vp, i64, i64, vp, i32, vp], None),
+            "orc_fp8_reencode": ([vp, vp, i64, i64, vp, vp], i64),
+            "orc_gemv_fp8r": ([vp, vp, i64, i64, vp, i32, vp], None),
             "orc_moe_accumulate": ([vp, vp, f32, i64], None),
         }
         for name, (args, res) in sig.items():
@@ -98,12 +103,46 @@ def _f32(a) -> np.ndarray:
 
 # ---- thin op wrappers (numpy in, numpy out) ----------------------------------------------------
 
+class FP8RTensor:
+    """FP8 E4M3 values [N][K] with one bf16 scale per 256 consecutive elements of a row [N][K/256]."""
+
+    def __init__(self, fp8: np.ndarray, bscale: np.ndarray):
+        self.fp8, self.bscale = fp8, bscale
+
+
+def fp8_reencode(W) -> FP8RTensor:
+    """The loader's lossless re-encoding of an MXFP4 gate or up matrix into FP8 with a bf16 scale per 256
+    (orc_fp8_reencode); raises when it is not lossless, as the loader does."""
+    codes, scales = np.ascontiguousarray(W.codes), np.ascontiguousarray(W.scales)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    fp8 = np.empty((N, K), dtype=np.uint8)
+    bs = np.empty((N, K // 256), dtype=np.uint16)
+    bad = lib().orc_fp8_reencode(_p(codes), _p(scales), N, K, _p(fp8), _p(bs))
+    if bad:
+        raise ValueError(f"FP8 re-encoding of an MXFP4 matrix is not lossless ({bad} elements differ)")
+    return FP8RTensor(fp8, bs)
+
+
 def gemv(W, X: np.ndarray) -> np.ndarray:
-    """Y[b] = W X[b]; W is bf16 bits [N][K] or an NVFP4 tensor (codes/scales/tensor_scale)."""
+    """Y[b] = W X[b]; W is bf16 bits [N][K], an NVFP4 tensor (codes/scales/tensor_scale), an MXFP4 tensor
+    (codes/scales, format "mxfp4") or an FP8 re-encoding (FP8RTensor)."""
     X = _f32(X)
     if X.ndim == 1:
         return gemv(W, X[None, :])[0]
     B, K = X.shape
+    if isinstance(W, FP8RTensor):
+        N = W.fp8.shape[0]
+        assert W.fp8.shape[1] == K
+        Y = np.empty((B, N), dtype=np.float32)
+        lib().orc_gemv_fp8r(_p(W.fp8), _p(W.bscale), N, K, _p(X), B, _p(Y))
+        return Y
+    if getattr(W, "format", None) == "mxfp4":
+        codes, scales = np.ascontiguousarray(W.codes), np.ascontiguousarray(W.scales)
+        N = codes.shape[0]
+        assert codes.shape[1] * 2 == K
+        Y = np.empty((B, N), dtype=np.float32)
+        lib().orc_gemv_mxfp4(_p(codes), _p(scales), N, K, _p(X), B, _p(Y))
+        return Y
     if hasattr(W, "codes"):
         N = W.codes.shape[0]
         assert W.codes.shape[1] * 2 == K
@@ -235,10 +274,19 @@ def argmax(x: np.ndarray) -> int:
 
 # ---- the step ----------------------------------------------------------------------------------
 
-def _swiglu(W, pre: str, y: np.ndarray) -> np.ndarray:
-    """SwiGLU FFN: W_d (silu(W_g y) * (W_u y))."""
-    g = gemv(W[pre + "wg"], y)
-    u = gemv(W[pre + "wu"], y)
+def _swiglu(W, pre: str, y: np.ndarray, reencoded: Optional[dict] = None) -> np.ndarray:
+    """SwiGLU FFN: W_d (silu(W_g y) * (W_u y)). MXFP4 experts take gate and up through their FP8
+    re-encoding and down as MXFP4 (page "Kimi K3's TPU megakernel ...", section "How it maps onto a TPU
+    v7", the precision paragraph); `reencoded` caches the re-encodings within one FFN evaluation."""
+    wg, wu = W[pre + "wg"], W[pre + "wu"]
+    if getattr(wg, "format", None) == "mxfp4":
+        if reencoded is None:
+            reencoded = {}
+        if pre not in reencoded:
+            reencoded[pre] = (fp8_reencode(wg), fp8_reencode(wu))
+        wg, wu = reencoded[pre]
+    g = gemv(wg, y)
+    u = gemv(wu, y)
     return gemv(W[pre + "wd"], silu_mul(g, u))
 
 
@@ -253,14 +301,15 @@ def _ffn(cfg, W, l: int, y: np.ndarray, route_log: Optional[dict]) -> np.ndarray
     out = np.zeros_like(y)
     idxs = np.empty((B, cfg.top_k), dtype=np.int32)
     gws = np.empty((B, cfg.top_k), dtype=np.float32)
+    reencoded: dict = {}
     for b in range(B):
         idx, gw = topk(z[b], cfg.top_k)
         idxs[b], gws[b] = idx, gw
         acc = np.zeros(cfg.hidden, dtype=np.float32)
         for s in range(cfg.n_shared):
-            moe_accumulate(acc, _swiglu(W, f"l{l}.s{s}.", y[b]), 1.0)
+            moe_accumulate(acc, _swiglu(W, f"l{l}.s{s}.", y[b], reencoded), 1.0)
         for t in range(cfg.top_k):
-            moe_accumulate(acc, _swiglu(W, f"l{l}.e{int(idx[t])}.", y[b]), float(gw[t]))
+            moe_accumulate(acc, _swiglu(W, f"l{l}.e{int(idx[t])}.", y[b], reencoded), float(gw[t]))
         out[b] = acc
     if route_log is not None:
         route_log[l] = (idxs, gws, z, y)  # y: the router's input, for the callers' rounding bounds

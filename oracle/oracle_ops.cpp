@@ -15,6 +15,7 @@
 // every product is rounded to fp32 and every sum is accumulated sequentially in index order in fp32
 // (built with -ffp-contract=off, so no multiply-add is fused). OpenMP splits only independent output
 // rows, so results are identical for any thread count.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -96,6 +97,112 @@ void orc_gemv_nvfp4(const uint8_t* codes, const uint8_t* scales, float tensor_sc
   for (int64_t n = 0; n < N; ++n) {
     std::vector<float> w((size_t)K);
     orc_nvfp4_dequant_row(codes + n * (K / 2), scales + n * (K / 16), tensor_scale, K, w.data());
+    for (int b = 0; b < B; ++b) {
+      const float* x = X + (int64_t)b * K;
+      float acc = 0.0f;
+      for (int64_t k = 0; k < K; ++k) acc += w[(size_t)k] * x[k];
+      Y[(int64_t)b * N + n] = acc;
+    }
+  }
+}
+
+// ---- MXFP4 (FP4 E2M1 values, E8M0 scale per 32 elements) and its FP8 re-encoding ---------------
+// E8M0: an 8-bit biased exponent, value 2^(e - 127); 0xFF is NaN (OCP Microscaling Formats v1.0).
+float orc_e8m0_value(uint8_t e) {
+  if (e == 0xFF) return std::nanf("");
+  return std::ldexp(1.0f, (int)e - 127);
+}
+
+// One row of K weights: element j = e2m1(code_j) * 2^(e_{j/32} - 127), exact in fp32.
+void orc_mxfp4_dequant_row(const uint8_t* codes, const uint8_t* scales, int64_t K, float* out) {
+  for (int64_t j = 0; j < K; ++j) {
+    uint8_t byte = codes[j / 2];
+    uint8_t nib = (j & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+    out[j] = orc_e2m1_value(nib) * orc_e8m0_value(scales[j / 32]);
+  }
+}
+
+void orc_gemv_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, const float* X, int B, float* Y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    std::vector<float> w((size_t)K);
+    orc_mxfp4_dequant_row(codes + n * (K / 2), scales + n * (K / 32), K, w.data());
+    for (int b = 0; b < B; ++b) {
+      const float* x = X + (int64_t)b * K;
+      float acc = 0.0f;
+      for (int64_t k = 0; k < K; ++k) acc += w[(size_t)k] * x[k];
+      Y[(int64_t)b * N + n] = acc;
+    }
+  }
+}
+
+// E4M3 (OCP e4m3fn) code of a value that the format holds exactly, else of its nearest (ties to even,
+// saturating at 448); the caller checks exactness by decoding.
+static uint8_t orc_e4m3_encode(float v) {
+  const uint8_t sign = std::signbit(v) ? 0x80 : 0;
+  const float a = std::fabs(v);
+  if (a == 0.0f) return sign;
+  if (a >= 448.0f) return sign | 0x7E;
+  if (a < std::ldexp(1.0f, -6)) {  // subnormals: multiples of 2^-9 (8 * 2^-9 is the smallest normal)
+    return sign | (uint8_t)std::nearbyint(a * 512.0f);
+  }
+  int e;
+  const float f = std::frexp(a, &e);  // a = f * 2^e, f in [0.5, 1)
+  e -= 1;                              // a = (2 f) * 2^e
+  float q = std::nearbyint((2.0f * f - 1.0f) * 8.0f);  // three mantissa bits, ties to even
+  if (q == 8.0f) { q = 0.0f; e += 1; }
+  const int E = e + 7;
+  if (E > 15 || (E == 15 && q == 7.0f)) return sign | 0x7E;
+  return sign | (uint8_t)((E << 3) | (int)q);
+}
+
+// The loader's re-encoding of an MXFP4 gate or up matrix [N][K] into FP8 E4M3 values with one bf16
+// scale per 256 consecutive elements of a row (page "Kimi K3's TPU megakernel ...", section "How it maps
+// onto a TPU v7", the precision paragraph). Per (row, 256-block) the scale is the power of two
+// S = 2^(m - 133), m the largest E8M0 exponent among the block's 32-blocks that hold a nonzero code
+// (S = 1 for an all-zero block), so every element becomes e2m1 * 2^(e - m + 6) with |value| <= 6 * 2^6
+// = 384 <= 448. The re-encoding is lossless when decode(fp8) * S equals the MXFP4 value bit for bit for
+// every element; returns the number of elements where it does not (0: lossless).
+int64_t orc_fp8_reencode(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, uint8_t* fp8,
+                         uint16_t* bscale) {
+  int64_t bad = 0;
+  const int64_t KB = K / 256;
+  for (int64_t n = 0; n < N; ++n) {
+    std::vector<float> w((size_t)K);
+    orc_mxfp4_dequant_row(codes + n * (K / 2), scales + n * (K / 32), K, w.data());
+    for (int64_t kb = 0; kb < KB; ++kb) {
+      int m = -1;
+      for (int j = 0; j < 8; ++j) {
+        bool nz = false;
+        for (int e = 0; e < 32; ++e) nz |= w[(size_t)(kb * 256 + j * 32 + e)] != 0.0f;
+        if (nz) m = std::max(m, (int)scales[n * (K / 32) + kb * 8 + j]);
+      }
+      const float S = m < 0 ? 1.0f : std::ldexp(1.0f, m - 133);
+      const uint16_t sb = orc_f32_to_bf16(S);  // a power of two: exact in bf16
+      bscale[n * KB + kb] = sb;
+      const float Sd = orc_bf16_to_f32(sb);
+      for (int e = 0; e < 256; ++e) {
+        const int64_t j = kb * 256 + e;
+        const float v = w[(size_t)j];
+        const uint8_t c = orc_e4m3_encode(v / Sd);
+        fp8[n * K + j] = c;
+        const float back = orc_e4m3_value(c) * Sd;
+        uint32_t ub, uv;
+        std::memcpy(&ub, &back, 4);
+        std::memcpy(&uv, &v, 4);
+        if (ub != uv) ++bad;
+      }
+    }
+  }
+  return bad;
+}
+
+// Y[b][n] = sum_k (e4m3(fp8[n][k]) * bscale[n][k / 256]) * X[b][k]
+void orc_gemv_fp8r(const uint8_t* fp8, const uint16_t* bscale, int64_t N, int64_t K, const float* X, int B, float* Y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    std::vector<float> w((size_t)K);
+    for (int64_t k = 0; k < K; ++k) w[(size_t)k] = orc_e4m3_value(fp8[n * K + k]) * orc_bf16_to_f32(bscale[n * (K / 256) + k / 256]);
     for (int b = 0; b < B; ++b) {
       const float* x = X + (int64_t)b * K;
       float acc = 0.0f;

@@ -52,6 +52,10 @@ def _matrix_bytes(spec) -> float:
         return spec.numel * 2
     if spec.kind == "nvfp4":  # E2M1 codes (half a byte) + one E4M3 scale per 16 values + the tensor scale
         return spec.numel // 2 + spec.numel // 16 + 4
+    if spec.kind == "mxfp4":  # gate/up re-encoded to FP8 with a bf16 scale per 256; down kept in MXFP4
+        if spec.name.endswith(".wd"):
+            return mxfp4_bytes(spec.numel)
+        return fp8_rowscaled_bytes(spec.numel, 1)
     return 0
 
 

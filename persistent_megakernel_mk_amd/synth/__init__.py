@@ -64,7 +64,7 @@ class ModelConfig:
     top_k: int = 0
     expert_ffn: int = 0
     n_shared: int = 0
-    expert_format: str = "bf16"  # "bf16" | "nvfp4"
+    expert_format: str = "bf16"  # "bf16" | "nvfp4" | "mxfp4" (gate/up re-encoded to FP8 when loaded)
     ctx: int = 0  # cached positions 0..ctx-1; the new token sits at position ctx
     batch: int = 1
     eps: float = 1e-6
@@ -135,7 +135,7 @@ _reg(ModelConfig(name="c4s", n_layers=2, hidden=1024, vocab=0, mixers=("gqa",) *
 class TensorSpec:
     name: str
     shape: Tuple[int, ...]
-    kind: str  # "bf16" | "f32" | "nvfp4" | "i32"
+    kind: str  # "bf16" | "f32" | "nvfp4" | "mxfp4" | "i32"
     sigma: float = 0.0
     mean: float = 0.0
     valid_positions: int = -1  # caches: positions >= this are zero
@@ -278,6 +278,7 @@ def lib() -> ctypes.CDLL:
         L.synth_normal_f32.argtypes = [u64, u64, u64, i64, f32, f32, vp]
         L.synth_uniform_int.argtypes = [u64, u64, u64, i64, ctypes.c_uint32, vp]
         L.synth_nvfp4_encode.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.synth_mxfp4_encode.argtypes = [vp, i64, i64, vp, vp]
         _lib = L
     return _lib
 
@@ -327,6 +328,28 @@ def nvfp4_encode(w: np.ndarray) -> NVFP4Tensor:
     return NVFP4Tensor(codes, scales, float(ts[0]))
 
 
+@dataclass
+class MXFP4Tensor:
+    """MXFP4: FP4 E2M1 codes [rows][k/2] (element 2i low nibble), E8M0 scales [rows][k/32]."""
+    codes: np.ndarray
+    scales: np.ndarray
+    format: str = "mxfp4"
+
+    @property
+    def shape(self) -> Tuple[int, int]:
+        return (self.codes.shape[0], self.codes.shape[1] * 2)
+
+
+def mxfp4_encode(w: np.ndarray) -> MXFP4Tensor:
+    rows, k = w.shape
+    assert k % 32 == 0
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    codes = np.empty((rows, k // 2), dtype=np.uint8)
+    scales = np.empty((rows, k // 32), dtype=np.uint8)
+    lib().synth_mxfp4_encode(_ptr(w), rows, k, _ptr(codes), _ptr(scales))
+    return MXFP4Tensor(codes, scales)
+
+
 def generate(spec: TensorSpec, seed: int):
     """Materialise one tensor on the host as numpy (bf16 as uint16 bits)."""
     if spec.kind == "bf16":
@@ -339,6 +362,9 @@ def generate(spec: TensorSpec, seed: int):
     if spec.kind == "nvfp4":
         w = normal_f32(seed, spec.tid, spec.numel, spec.sigma, spec.mean).reshape(spec.shape)
         return nvfp4_encode(w)
+    if spec.kind == "mxfp4":
+        w = normal_f32(seed, spec.tid, spec.numel, spec.sigma, spec.mean).reshape(spec.shape)
+        return mxfp4_encode(w)
     raise ValueError(spec.kind)
 
 
@@ -454,3 +480,7 @@ def draft_tokens_other(cfg: ModelConfig, n: int) -> np.ndarray:
     return uniform_int(cfg.seed, tid, n, max(cfg.vocab - 1, 1))
 
 _reg(replace(CONFIGS["c4s"], name="c4s_bf16", expert_format="bf16", seed=2006))
+# the Kimi-class slice with the pages' expert formats: experts shipped in MXFP4, gate/up re-encoded to FP8
+# E4M3 with a bf16 scale per 256 when loaded, down kept in MXFP4
+_reg(replace(CONFIGS["c3"], name="c3m", expert_format="mxfp4", seed=1005))
+_reg(replace(CONFIGS["c3s"], name="c3ms", expert_format="mxfp4", seed=2008))

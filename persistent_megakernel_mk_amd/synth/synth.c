@@ -138,6 +138,38 @@ static uint8_t syn_e4m3_rne_pos(float a) {
   return (uint8_t)((E << 3) | (int)m);
 }
 
+/* MXFP4 encoding of seeded weights (Open Compute Project "OCP Microscaling Formats (MX) v1.0",
+ * the MXFP4 element format with its conversion recipe): per block of 32 consecutive values along a row,
+ * the shared E8M0 scale is X = 2^(floor(log2(amax)) - 2) (2 = the largest exponent of E2M1), and each
+ * element becomes the E2M1 code of v / X rounded to nearest even, saturating at 6. An all-zero block
+ * takes X = 2^-127 (code 0). Codes are packed as for NVFP4 (element 2i in the low nibble of byte i). */
+void synth_mxfp4_encode(const float *w, int64_t rows, int64_t k, uint8_t *codes, uint8_t *scales) {
+  const int64_t nb = k / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float *blk = w + r * k + b * 32;
+      float amax = 0.0f;
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(blk[e]));
+      int ex = 0;
+      if (amax > 0.0f) {
+        int e2;
+        frexpf(amax, &e2);                      /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+        ex = (e2 - 1) - 2 + 127;
+        if (ex < 0) ex = 0;
+        if (ex > 254) ex = 254;
+      }
+      scales[r * nb + b] = (uint8_t)ex;
+      const float X = ldexpf(1.0f, ex - 127);
+      for (int e = 0; e < 32; e += 2) {
+        uint8_t lo = amax > 0.0f ? syn_e2m1_rne(blk[e] / X) : 0;
+        uint8_t hi = amax > 0.0f ? syn_e2m1_rne(blk[e + 1] / X) : 0;
+        codes[r * (k / 2) + (b * 32 + e) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
 void synth_nvfp4_encode(const float *w, int64_t rows, int64_t k, uint8_t *codes, uint8_t *scales, float *tensor_scale) {
   float amax = 0.0f;
   for (int64_t i = 0; i < rows * k; ++i) amax = fmaxf(amax, fabsf(w[i]));
