@@ -52,13 +52,14 @@ def build_gpu(cfg, max_batch, expert_pool=8):
         layer, kind, expert = mk.weight_target(spec.name)
         d = mk.WeightDesc()
         d.layer, d.kind, d.expert = layer, kind, expert
-        if spec.kind == "nvfp4":
+        if spec.kind in ("nvfp4", "mxfp4"):
             key, src = pooled_source(cfg, spec, expert_pool)
             if key not in pool:
                 a = synth.generate(src, cfg.seed)
-                pool[key] = (torch.from_numpy(a.codes).cuda(), torch.from_numpy(a.scales).cuda(), float(a.tensor_scale))
+                pool[key] = (torch.from_numpy(a.codes).cuda(), torch.from_numpy(a.scales).cuda(),
+                             float(getattr(a, "tensor_scale", 1.0)))
             codes, scales, ts = pool[key]
-            d.dtype = mk.DTYPE["nvfp4"]
+            d.dtype = mk.DTYPE[spec.kind]
             d.rows, d.cols = spec.shape
             d.data, d.scales, d.tensor_scale = codes.data_ptr(), scales.data_ptr(), ts
             t = None
@@ -83,7 +84,7 @@ def build_gpu(cfg, max_batch, expert_pool=8):
     torch.cuda.synchronize()
     log(f"weights and states generated and packed in {time.time() - t0:.1f} s "
         f"({m.sizes.packed_weights / 1e9:.2f} GB packed"
-        + (f"; {n_fp4} NVFP4 matrices from a pool of {expert_pool} per projection" if n_fp4 else "") + ")")
+        + (f"; {n_fp4} {cfg.expert_format.upper()} matrices from a pool of {expert_pool} per projection" if n_fp4 else "") + ")")
     return m
 
 
@@ -293,6 +294,10 @@ def describe(cfg, batch):
         what = (f"Kimi-class slice decode step, {cfg.n_layers} layers (3 KDA : 1 absorbed MLA), hidden {cfg.hidden}, "
                 f"MoE {cfg.n_experts} experts top-{cfg.top_k} + {cfg.n_shared} shared (bf16, ffn {cfg.expert_ffn}), "
                 f"{cfg.ctx}-token latent cache")
+    elif cfg.name == "c3m":
+        what = (f"Kimi-class slice decode step, {cfg.n_layers} layers (3 KDA : 1 absorbed MLA), hidden {cfg.hidden}, "
+                f"MoE {cfg.n_experts} experts top-{cfg.top_k} + {cfg.n_shared} shared (MXFP4 shipped: gate/up re-encoded "
+                f"to FP8 E4M3 + bf16 scale per 256, down MXFP4; ffn {cfg.expert_ffn}), {cfg.ctx}-token latent cache")
     elif cfg.name == "c4":
         what = (f"NVFP4-expert slice decode step, {cfg.n_layers} GQA layers, hidden {cfg.hidden}, MoE {cfg.n_experts} "
                 f"experts top-{cfg.top_k} + {cfg.n_shared} shared (NVFP4, ffn {cfg.expert_ffn}), {cfg.ctx}-token KV cache")
@@ -476,7 +481,7 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    default_batches = {"c0": "1", "c1": "1,2,4,8,16", "c2": "1", "c3": "8", "c4": "1,4,8"}
+    default_batches = {"c0": "1", "c1": "1,2,4,8,16", "c2": "1", "c3": "8", "c3m": "8", "c4": "1,4,8"}
     batches = [int(b) for b in (args.batches or default_batches.get(args.config, "1,8")).split(",")]
     if args.calib_copy:
         src = torch.ones(args.calib_copy << 18, dtype=torch.float32, device="cuda")

@@ -52,12 +52,19 @@ typedef enum {
   MK_E_CAPACITY = 4,     /* batch > max_batch, position + rows > max_ctx, on-chip budget exceeded */
   MK_E_HIP = 5,          /* a HIP runtime call failed (message in mk_last_error) */
   MK_E_DEVICE_TIMEOUT = 6, /* an in-kernel wait expired (from mk_read_device_status) */
-  MK_E_STATE = 7         /* call out of order (e.g. a step before all buffers/weights are in place) */
+  MK_E_STATE = 7,        /* call out of order (e.g. a step before all buffers/weights are in place) */
+  MK_E_INEXACT = 8       /* a weight re-encoding the configuration asks for is not lossless (nothing kept) */
 } mk_status;
 
 typedef enum { MK_MIXER_GQA = 0, MK_MIXER_GDN = 1, MK_MIXER_KDA = 2, MK_MIXER_MLA = 3 } mk_mixer;
 typedef enum { MK_FFN_DENSE = 0, MK_FFN_MOE = 1 } mk_ffn_kind;
-typedef enum { MK_DT_BF16 = 0, MK_DT_NVFP4 = 1 } mk_dtype;
+/* Weight element formats. MK_DT_MXFP4 (expert matrices only): FP4 E2M1 codes [rows][cols/2] (element 2i
+ * in the low nibble of byte i) with an E8M0 scale per 32 consecutive elements of a row [rows][cols/32]
+ * (OCP Microscaling). A configuration whose experts are MXFP4 keeps down in MXFP4 and re-encodes gate and
+ * up at load time into FP8 E4M3 with one bf16 scale per 256 elements of a row, checking that the new
+ * encoding decodes to the same values bit for bit (page "Kimi K3's TPU megakernel: 92 layers in one Pallas
+ * call, and what 709 tokens a second measures", section "How it maps onto a TPU v7"). */
+typedef enum { MK_DT_BF16 = 0, MK_DT_NVFP4 = 1, MK_DT_MXFP4 = 2 } mk_dtype;
 
 /* Model configuration. A layer is RMSNorm -> mixer -> residual add -> RMSNorm -> FFN -> residual add.
  * vocab > 0: the step embeds tokens and ends with a final RMSNorm and LM head (logits out).
@@ -151,7 +158,10 @@ mk_status mk_bind_buffers(mk_ctx *ctx, const mk_buffers *bufs);
 
 /* Copies n weight tensors into the packed buffer, converting each to the kernel's tile-major layout
  * (asynchronous on stream). Every tensor the configuration needs must be loaded once before the first
- * step; loading a tensor again replaces it. */
+ * step; loading a tensor again replaces it. MXFP4 gate and up matrices are re-encoded to FP8 E4M3 with a
+ * power-of-two bf16 scale per 256 elements of a row; when any of them has an element without an exact
+ * E4M3 value at its block's scale, the call waits for the stream and returns MK_E_INEXACT, and those
+ * matrices count as not loaded (a step refuses to run until they are loaded again). */
 mk_status mk_load_weights(mk_ctx *ctx, const mk_weight_desc *w, int n, void *hip_stream);
 
 /* One decode step for `batch` sequences (1 <= batch <= max_batch) as one persistent kernel launch on

@@ -282,9 +282,10 @@ def _swiglu(W, pre: str, y: np.ndarray, reencoded: Optional[dict] = None) -> np.
     if getattr(wg, "format", None) == "mxfp4":
         if reencoded is None:
             reencoded = {}
-        if pre not in reencoded:
-            reencoded[pre] = (fp8_reencode(wg), fp8_reencode(wu))
-        wg, wu = reencoded[pre]
+        key = (id(wg), id(wu))  # the entry keeps both sources alive, so their identities stay unique
+        if key not in reencoded:
+            reencoded[key] = (wg, wu, fp8_reencode(wg), fp8_reencode(wu))
+        wg, wu = reencoded[key][2:]
     g = gemv(wg, y)
     u = gemv(wu, y)
     return gemv(W[pre + "wd"], silu_mul(g, u))

@@ -167,6 +167,7 @@ int64_t orc_fp8_reencode(const uint8_t* codes, const uint8_t* scales, int64_t N,
                          uint16_t* bscale) {
   int64_t bad = 0;
   const int64_t KB = K / 256;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
   for (int64_t n = 0; n < N; ++n) {
     std::vector<float> w((size_t)K);
     orc_mxfp4_dequant_row(codes + n * (K / 2), scales + n * (K / 32), K, w.data());

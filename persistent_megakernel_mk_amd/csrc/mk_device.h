@@ -322,18 +322,25 @@ __device__ __forceinline__ void compute_route(CArgs &a, const Phase &ph, char *s
 }
 
 // The weight stream of one compute wave: the wave's share of every product phase, in phase order.
-// An item is one 1 KiB load per wave: a bf16 fragment (16 rows x 32 columns), or for NVFP4 the codes
-// of four fragments (16 rows x 128 columns) together with a 128-byte load of their E4M3 scales.
+// An item is one 1 KiB load per wave: a bf16 fragment (16 rows x 32 columns); for NVFP4 or MXFP4 the
+// codes of four fragments (16 rows x 128 columns) with a load of their scales (128 B of E4M3, or 64 B of
+// E8M0); for FP8 the values of two fragments (16 rows x 64 columns) with a load of the bf16 scales of
+// their 256-column block (32 B, shared by the block's four items).
 struct Stream {
   const uint4 *ptr;        // next item (or a valid dummy address once the stream is done)
-  const uint32_t *sptr;    // its scales (NVFP4) or a fixed dummy word
-  int q, left, j, nfw, skip, sstep;  // phase, units left, item in run, items per run, items between runs
+  const uint32_t *sptr;    // its scales, or a fixed dummy word
+  int q, left, j, nfw, skip, sstep;  // phase, units left, item in run, items per run, items between runs,
+                                     // scale words per item (NVFP4 32, MXFP4 16; 0: none or FP8)
   int seg, seg_left;       // current segment, units left in it
   int route_q;             // routing this workgroup holds (phase index of its expert gate/up product)
   int blocked;             // expert phase the stream waits at until the routing is known (-1: none)
+  int fmt;                 // WeightFmt of the current phase
+  int kpos, kpos0;         // FP8: item index along the tile's row (current, first of the run)
+  int tile_words;          // FP8: scale words per tile
+  const uint32_t *sbase;   // FP8: the current tile's scales
 };
 
-__device__ __forceinline__ int items_per_frag_row(const Phase &ph) { return ph.fmt == FMT_NVFP4 ? ph.KF / 4 : ph.KF; }
+__device__ __forceinline__ int items_per_frag_row(const Phase &ph) { return ph.KF / frags_per_item(ph.fmt); }
 
 // The compute waves' shares of the n items of a k-split: contiguous runs, the first n % 4 waves one
 // item longer (the schedule makes n a multiple of 4 up to kMaxRows rows; above, any n >= 4).
@@ -343,17 +350,25 @@ __device__ __forceinline__ int wave_first(int n, int w) { return w * (n / kCWave
 // first item of segment seg, tile t (its own weight block for expert phases), this wave's run
 __device__ __forceinline__ void stream_at(Stream &st, CArgs &a, CPhase *ph, const char *smem, int s, int seg,
                                           int t, int wave) {
-  const int KI = ph->fmt == FMT_NVFP4 ? ph->KF / 4 : ph->KF;
-  const int nfi = ph->fmt == FMT_NVFP4 ? ph->nf / 4 : ph->nf;
+  const int fpi = frags_per_item(ph->fmt);
+  const int KI = ph->KF / fpi, nfi = ph->nf / fpi;
   const uint8_t *base = a.wbuf + ph->w_off;
   int64_t tile = t;
   if (ph->seg == SEG_EXPERT) base += (int64_t)__builtin_amdgcn_readfirstlane(route_lds(smem)->expert[seg]) * ph->seg_stride;
   else tile += (int64_t)seg * ph->seg_T;
   const int64_t item = tile * KI + s * nfi + wave_first(nfi, wave);
   st.ptr = reinterpret_cast<const uint4 *>(base) + item * 64;
-  if (ph->fmt == FMT_NVFP4) {
+  if (ph->fmt != FMT_BF16) {  // the scales follow the matrix's codes
     const int Tm = ph->seg == SEG_EXPERT ? ph->seg_T : ph->T;
-    st.sptr = reinterpret_cast<const uint32_t *>(base + (int64_t)Tm * KI * 1024) + item * 32;
+    const uint32_t *sc = reinterpret_cast<const uint32_t *>(base + (int64_t)Tm * KI * 1024);
+    if (ph->fmt == FMT_FP8R) {  // [tile][256-column block][16 rows] bf16: 8 words per (tile, block)
+      st.tile_words = (KI / 4) * 8;
+      st.sbase = sc + tile * st.tile_words;
+      st.kpos = st.kpos0 = s * nfi + wave_first(nfi, wave);
+      st.sptr = st.sbase + (st.kpos >> 2) * 8;
+    } else {
+      st.sptr = sc + item * st.sstep;
+    }
   }
 }
 
@@ -364,6 +379,7 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
   st.ptr = reinterpret_cast<const uint4 *>(a.wbuf);
   st.sptr = reinterpret_cast<const uint32_t *>(a.wbuf);
   st.sstep = 0;
+  st.fmt = FMT_BF16;  // no scale loads while the stream is done or blocked
   while (q >= 0 && q < a.phase_end) {
     CPhase *ph = cphase(a, q);
     if (ph->type == PH_GEMV) {
@@ -375,14 +391,15 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
       int s, u0, u1;
       unit_range(U, ph->S, s, u0, u1);
       if (u1 > u0) {
-        const bool fp4 = ph->fmt == FMT_NVFP4;
-        const int nfi = fp4 ? ph->nf / 4 : ph->nf;
+        const int fpi = frags_per_item(ph->fmt);
+        const int nfi = ph->nf / fpi;
         st.q = q;
         st.nfw = wave_items(nfi, wave);
         st.left = u1 - u0;
         st.j = 0;
-        st.skip = (fp4 ? ph->KF / 4 : ph->KF) - st.nfw;
-        st.sstep = fp4 ? 32 : 0;
+        st.skip = ph->KF / fpi - st.nfw;
+        st.fmt = ph->fmt;
+        st.sstep = ph->fmt == FMT_NVFP4 ? 32 : (ph->fmt == FMT_MXFP4 ? 16 : 0);
         const int sT = ph->seg == SEG_EXPERT ? ph->seg_T : 0x40000000;
         st.seg = ph->seg == SEG_EXPERT ? u0 / sT : 0;
         int t = ph->seg == SEG_EXPERT ? u0 - st.seg * sT : u0;
@@ -407,10 +424,19 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
 __device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *smem, int wave, int lane,
                                             uint4 &v, uint32_t &sv) {
   v = ld_nt(st.ptr + lane);
-  if (st.sstep) sv = __builtin_nontemporal_load(st.sptr + ((lane & 15) + 16 * (lane >> 5)));
+  if (st.fmt != FMT_BF16) {
+    // the scale word of this lane's row: NVFP4 per half of the lane groups, MXFP4 one per row, FP8 two
+    // rows' bf16 per word
+    const int sidx = st.fmt == FMT_NVFP4 ? (lane & 15) + 16 * (lane >> 5) : (st.fmt == FMT_MXFP4 ? lane & 15 : (lane & 15) >> 1);
+    sv = __builtin_nontemporal_load(st.sptr + sidx);
+  }
   if (st.q >= 0) {
     st.ptr += 64;
-    st.sptr += st.sstep;
+    if (st.fmt == FMT_FP8R) {
+      if ((++st.kpos & 3) == 0) st.sptr += 8;  // the next 256-column block
+    } else {
+      st.sptr += st.sstep;
+    }
     if (++st.j == st.nfw) {
       st.j = 0;
       if (--st.left == 0) {
@@ -431,7 +457,13 @@ __device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *sm
         }
       } else {
         st.ptr += (int64_t)st.skip * 64;
-        st.sptr += (int64_t)st.skip * st.sstep;
+        if (st.fmt == FMT_FP8R) {  // the run of the next tile
+          st.kpos = st.kpos0;
+          st.sbase += st.tile_words;
+          st.sptr = st.sbase + (st.kpos >> 2) * 8;
+        } else {
+          st.sptr += (int64_t)st.skip * st.sstep;
+        }
       }
     }
   }
@@ -659,6 +691,19 @@ __device__ __forceinline__ bf16x8 nvfp4_frag(uint32_t codes, float scale) {
   return bf16x8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
 }
 
+// E8M0 scale byte -> fp32: 2^(e - 127) (e = 0 gives the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
+
+// Eight FP8 E4M3 weights of one lane (bytes of lo, then hi) times their power-of-two bf16 block scale ->
+// bf16 (exact: an E4M3 value has four significant bits).
+__device__ __forceinline__ bf16x8 fp8_frag(uint32_t lo, uint32_t hi, float scale) {
+  f32x2 p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  f32x2 p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  bf16x2 b0 = __builtin_convertvector(p0 * scale, bf16x2), b1 = __builtin_convertvector(p1 * scale, bf16x2);
+  bf16x2 b2 = __builtin_convertvector(p2 * scale, bf16x2), b3 = __builtin_convertvector(p3 * scale, bf16x2);
+  return bf16x8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
+
 // compute waves: consume this phase's items from the ring, refilling each slot from the stream.
 // A finished 16-row unit is handed to the sync wave through an LDS slot and a counter, without a
 // workgroup barrier, so the four waves never wait for each other inside a phase.
@@ -667,9 +712,12 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
                                          Stream &st, int &head, int s, int u0, int u1) {
   const int R = a.R;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const bool FP4 = HAS_FP4 && ph.fmt == FMT_NVFP4;
-  const int nfw = wave_items(ph.nf, wave);        // fragments per unit run of this wave (NVFP4: a multiple of 4)
-  const int ipr = FP4 ? nfw / 4 : nfw;            // ring items per unit run
+  const bool FP4 = HAS_FP4 && (ph.fmt == FMT_NVFP4 || ph.fmt == FMT_MXFP4);  // four FP4 fragments per item
+  const bool MX = HAS_FP4 && ph.fmt == FMT_MXFP4;                             // their scales: E8M0, else E4M3
+  const bool FP8 = HAS_FP4 && ph.fmt == FMT_FP8R;                             // two FP8 fragments per item
+  const int nfw = wave_items(ph.nf, wave);        // fragments per unit run of this wave (a multiple of the
+                                                  // fragments per item)
+  const int ipr = FP4 ? nfw / 4 : (FP8 ? nfw / 2 : nfw);  // ring items per unit run
   const int total = (u1 - u0) * ipr;
   float *red = reinterpret_cast<float *>(smem + GemvLds::red);
   uint32_t *posted = reinterpret_cast<uint32_t *>(smem + GemvLds::flags);
@@ -718,9 +766,28 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
   };
   // one ring item: MFMA(s) with the activation fragment(s), refill the slot from the stream
   auto slot = [&](uint4 &r, uint32_t &sc) {
-    if (FP4) {
-      const float sc4[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sc, 0), __builtin_amdgcn_cvt_f32_fp8((int)sc, 1),
-                            __builtin_amdgcn_cvt_f32_fp8((int)sc, 2), __builtin_amdgcn_cvt_f32_fp8((int)sc, 3)};
+    if (FP8) {  // the lane's row scale: half (lane & 1) of the scale word
+      const float s8 = __uint_as_float(((sc >> ((lane & 1) * 16)) & 0xFFFFu) << 16);
+      const uint32_t cw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        uint4 bv = uint4{0u, 0u, 0u, 0u};
+        if (col < 2 * R) bv = aw[((c_j * 2 + f) * 4 + kgrp) * C + col];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_frag(cw[2 * f], cw[2 * f + 1], s8), __builtin_bit_cast(bf16x8, bv),
+                                                      acc, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);  // one fragment's dequantised weights live at a time
+      }
+    } else if (FP4) {
+      float sc4[4];
+      if (MX) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) sc4[f] = e8m0_f32((sc >> (8 * f)) & 255u);
+      } else {
+        sc4[0] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
+        sc4[1] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
+        sc4[2] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 2);
+        sc4[3] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 3);
+      }
       const uint32_t cw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
       for (int f = 0; f < 4; ++f) {

@@ -31,6 +31,10 @@ extern "C" __global__ void mk_repack_bf16(const uint16_t *src, int64_t rows, int
 extern "C" __global__ void mk_repack_nvfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
                                            int64_t row_off, int64_t dst_rows);
 extern "C" __global__ void mk_store_f32(float *dst, float v);
+extern "C" __global__ void mk_repack_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
+                                           int64_t row_off, int64_t dst_rows);
+extern "C" __global__ void mk_reencode_fp8(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *dst,
+                                           int64_t row_off, int64_t dst_rows, uint32_t *inexact);
 
 // ---------------------------------------------------------------------------------------------
 // Library-held working memory of mk_decode_step_noalloc: one array per GPU, part of this code object
@@ -106,7 +110,20 @@ struct LayerSlots {
 // Bytes of one packed matrix: bf16, or NVFP4 codes (half a byte per weight) plus one E4M3 scale per
 // 16 weights.
 int64_t matrix_bytes(int64_t rows, int64_t cols, int fmt) {
-  return fmt == FMT_NVFP4 ? rows * cols / 2 + rows * cols / 16 : rows * cols * 2;
+  switch (fmt) {
+    case FMT_NVFP4: return rows * cols / 2 + rows * cols / 16;  // codes + an E4M3 scale per 16
+    case FMT_MXFP4: return rows * cols / 2 + rows * cols / 32;  // codes + an E8M0 scale per 32
+    case FMT_FP8R: return rows * cols + rows * cols / 128;      // E4M3 + a bf16 scale per 256
+    default: return rows * cols * 2;
+  }
+}
+
+// Stream formats of an expert layer's gate|up and down matrices for the configured expert format.
+int gate_up_fmt(const mk_config &f) {
+  return f.expert_format == MK_DT_NVFP4 ? FMT_NVFP4 : (f.expert_format == MK_DT_MXFP4 ? FMT_FP8R : FMT_BF16);
+}
+int down_fmt(const mk_config &f) {
+  return f.expert_format == MK_DT_NVFP4 ? FMT_NVFP4 : (f.expert_format == MK_DT_MXFP4 ? FMT_MXFP4 : FMT_BF16);
 }
 
 struct Schedule {
@@ -184,8 +201,9 @@ mk_status validate(const mk_config *c) {
     if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_experts)
       return fail(MK_E_UNSUPPORTED, "top_k %d out of [1, min(%d, n_experts)]", c->top_k, kMaxTopK);
     if (c->n_shared < 0 || c->n_shared > kMaxShared) return fail(MK_E_UNSUPPORTED, "n_shared %d out of [0, %d]", c->n_shared, kMaxShared);
-    if (c->expert_format != MK_DT_BF16 && c->expert_format != MK_DT_NVFP4) return fail(MK_E_ARG, "bad expert_format %d", c->expert_format);
-    const int q = c->expert_format == MK_DT_NVFP4 ? 512 : 256;
+    if (c->expert_format != MK_DT_BF16 && c->expert_format != MK_DT_NVFP4 && c->expert_format != MK_DT_MXFP4)
+      return fail(MK_E_ARG, "bad expert_format %d", c->expert_format);
+    const int q = c->expert_format == MK_DT_BF16 ? 256 : 512;
     if (c->expert_ffn <= 0 || c->expert_ffn % q || c->hidden % q)
       return fail(MK_E_UNSUPPORTED, "expert_ffn %d and hidden %d must be positive multiples of %d", c->expert_ffn, c->hidden, q);
   }
@@ -224,13 +242,14 @@ mk_status validate(const mk_config *c) {
 // the LDS budget, and the fewest fragment-slots on the busiest workgroup (plus about one fragment's
 // time per unit for the cross-wave reduction). A product of nseg segments of segT tiles each gives every
 // segment its own activation when per_seg_act (one piece per segment a workgroup's units touch).
-int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_seg_act = false, bool fp4 = false,
+int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_seg_act = false, int fpi = 1,
                   int *pieces_out = nullptr, bool resid = false) {
   int best = -1, best_pieces = 1;
   double best_cost = 1e300;
   const int64_t U = (int64_t)segT * nseg;
-  const int q = fp4 ? 4 * kCWaves : kCWaves;
-  const bool uneven = !fp4 && R > kMaxRows;
+  if (fpi != 1 && fpi != 2 && fpi != 4) return -1;
+  const int q = fpi * kCWaves;  // fpi: fragments per stream item (1 bf16, 2 FP8, 4 NVFP4 / MXFP4)
+  const bool uneven = fpi == 1 && R > kMaxRows;
   for (int S = 1; S <= KF / q && S <= G; S *= 2) {
     if (KF % S || (!uneven && (KF / S) % q) || S > max_S || G % S) continue;
     const int nf = KF / S;
@@ -262,7 +281,7 @@ Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S) {
   p.K = w.K;
   p.T = w.N / kTileRows;
   p.KF = w.K / kFragK;
-  p.S = choose_splits(p.T, 1, p.KF, R, G, max_S, false, false, nullptr, resid);
+  p.S = choose_splits(p.T, 1, p.KF, R, G, max_S, false, 1, nullptr, resid);
   p.nf = p.S > 0 ? p.KF / p.S : 0;
   p.act = act;
   p.out = out;
@@ -362,7 +381,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       ak.src_N = p.N;
       ak.src_off = s.q_off;
       ak.src_seg = f.nope_dim + f.rope_dim;
-      ak.S = choose_splits(ak.seg_T, hq, ak.KF, R, G, 1, true, false, &ak.pieces);
+      ak.S = choose_splits(ak.seg_T, hq, ak.KF, R, G, 1, true, 1, &ak.pieces);
       ak.nf = ak.S > 0 ? ak.KF / ak.S : 0;
       if (mk_status st = add_gemv(ak, 2)) return st;
       mx.type = PH_MLA;
@@ -388,7 +407,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       av.seg_T = f.v_dim / kTileRows;
       av.src_off = 0;
       av.src_seg = rank;
-      av.S = choose_splits(av.seg_T, hq, av.KF, R, G, 64, true, false, &av.pieces);
+      av.S = choose_splits(av.seg_T, hq, av.KF, R, G, 64, true, 1, &av.pieces);
       av.nf = av.S > 0 ? av.KF / av.S : 0;
       if (mk_status st = add_gemv(av, 0)) return st;
       Phase o = gemv_phase(s.wo, ACT_PART, OUT_RESID, R, G, 68);
@@ -428,7 +447,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       // mixture of experts: router logits; gate|up of the shared experts and the batch's routed union
       // (every workgroup derives the union from the logits); down of the same segments, each row's
       // activation scaled by its routing weight, summed into the residual
-      const bool fp4 = f.expert_format == MK_DT_NVFP4;
+      const int fmt_gu = gate_up_fmt(f), fmt_d = down_fmt(f);
       const int F = f.expert_ffn, H = f.hidden;
       const int nseg_max = f.n_shared + std::min(f.n_experts, R * f.top_k);
       Phase r = gemv_phase(s.router, ACT_NORM, OUT_PART, R, G, 64);
@@ -440,7 +459,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       gu.type = PH_GEMV;
       gu.layer = l;
       gu.seg = SEG_EXPERT;
-      gu.fmt = fp4 ? FMT_NVFP4 : FMT_BF16;
+      gu.fmt = fmt_gu;
       gu.w_off = s.ex_gu_off;
       gu.seg_stride = s.ex_gu_bytes;
       gu.seg_T = 2 * F / kTileRows;
@@ -449,7 +468,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       gu.K = H;
       gu.T = gu.N / kTileRows;
       gu.KF = H / kFragK;
-      gu.S = choose_splits(gu.seg_T, nseg_max, gu.KF, R, G, 64, false, fp4, &gu.pieces);
+      gu.S = choose_splits(gu.seg_T, nseg_max, gu.KF, R, G, 64, false, frags_per_item(fmt_gu), &gu.pieces);
       gu.nf = gu.S > 0 ? gu.KF / gu.S : 0;
       gu.act = ACT_NORM;
       gu.gain_off = s.ffn_norm.off;
@@ -472,7 +491,8 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       d.K = F;
       d.T = d.seg_T;
       d.KF = F / kFragK;
-      d.S = choose_splits(d.seg_T, nseg_max, d.KF, R, G, 64, true, fp4, &d.pieces);
+      d.fmt = fmt_d;
+      d.S = choose_splits(d.seg_T, nseg_max, d.KF, R, G, 64, true, frags_per_item(fmt_d), &d.pieces);
       d.nf = d.S > 0 ? d.KF / d.S : 0;
       d.act = ACT_SWIGLU;
       d.gain_off = 0;
@@ -580,12 +600,11 @@ mk_status layout(mk_ctx *c) {
       place(s.gu, 2 * f.ffn, H, true);
       place(s.wd, H, f.ffn, true);
     } else {
-      const int fmt = f.expert_format == MK_DT_NVFP4 ? FMT_NVFP4 : FMT_BF16;
       const int64_t nblk = (int64_t)f.n_experts + f.n_shared;
       s.need |= kind_bit(MK_W_ROUTER);
       place(s.router, (int)round16(f.n_experts), H, true);
-      s.ex_gu_bytes = align_up(matrix_bytes(2LL * f.expert_ffn, H, fmt), 256);
-      s.ex_down_bytes = align_up(matrix_bytes(H, f.expert_ffn, fmt), 256);
+      s.ex_gu_bytes = align_up(matrix_bytes(2LL * f.expert_ffn, H, gate_up_fmt(f)), 256);
+      s.ex_down_bytes = align_up(matrix_bytes(H, f.expert_ffn, down_fmt(f)), 256);
       s.ex_gu_off = off;
       off += nblk * s.ex_gu_bytes;
       s.ex_down_off = off;
@@ -668,7 +687,6 @@ mk_status resolve(mk_ctx *c, const mk_weight_desc &w, Slot **slot, int64_t *row_
       return fail(MK_E_ARG, "layer %d: expert index %d out of range", w.layer, w.expert);
     LayerSlots &s = c->L[w.layer];
     const int F = f0.expert_ffn, H = f0.hidden;
-    tg->fmt = f0.expert_format == MK_DT_NVFP4 ? FMT_NVFP4 : FMT_BF16;
     int which;
     switch (w.kind) {
       case MK_W_GATE: which = 0; *rows = F; *cols = H; *row_off = 0; break;
@@ -676,6 +694,7 @@ mk_status resolve(mk_ctx *c, const mk_weight_desc &w, Slot **slot, int64_t *row_
       case MK_W_DOWN: which = 2; *rows = H; *cols = F; *row_off = 0; break;
       default: return fail(MK_E_ARG, "layer %d: kind %d is not an expert tensor", w.layer, w.kind);
     }
+    tg->fmt = which < 2 ? gate_up_fmt(f0) : down_fmt(f0);
     tg->off = which < 2 ? s.ex_gu_off + (int64_t)blk * s.ex_gu_bytes : s.ex_down_off + (int64_t)blk * s.ex_down_bytes;
     tg->mrows = which < 2 ? 2LL * F : H;
     tg->ts_off = s.ts_off + ((int64_t)blk * 3 + which) * 4;
@@ -956,7 +975,7 @@ mk_status mk_create(const mk_config *cfg, int hip_device, mk_ctx **out) {
   c->device = hip_device;
   c->max_rows = cfg->vocab > 0 ? std::max(kMaxRows, cfg->max_batch) : cfg->max_batch;  // verify blocks have kMaxRows rows
   for (int l = 0; l < cfg->n_layers; ++l)
-    if (cfg->ffn_kind[l] == MK_FFN_MOE && cfg->expert_format == MK_DT_NVFP4) c->nvfp4 = true;
+    if (cfg->ffn_kind[l] == MK_FFN_MOE && cfg->expert_format != MK_DT_BF16) c->nvfp4 = true;
   if (hip_device >= 0) {
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, hip_device);
@@ -1089,7 +1108,7 @@ mk_status mk_load_weights(mk_ctx *c, const mk_weight_desc *w, int n, void *strea
     uint32_t *have;
     Target tg;
     if (mk_status s = resolve(c, w[i], &slot, &ro, &rows, &cols, &have, &tg)) return s;
-    const int want = tg.off >= 0 && tg.fmt == FMT_NVFP4 ? MK_DT_NVFP4 : MK_DT_BF16;
+    const int want = tg.off >= 0 ? c->cfg.expert_format : MK_DT_BF16;
     if (w[i].dtype != want)
       return fail(MK_E_UNSUPPORTED, "tensor %d (layer %d kind %d): dtype %d, this configuration stores it as %d", i, w[i].layer,
                   w[i].kind, w[i].dtype, want);
@@ -1101,8 +1120,14 @@ mk_status mk_load_weights(mk_ctx *c, const mk_weight_desc *w, int n, void *strea
       if (!w[i].scales) return fail(MK_E_ARG, "tensor %d: NVFP4 scales are required", i);
       if (!(std::isfinite(w[i].tensor_scale))) return fail(MK_E_ARG, "tensor %d: tensor scale must be finite", i);
     }
+    if (want == MK_DT_MXFP4 && (!w[i].scales || ((uintptr_t)w[i].scales & 3)))
+      return fail(MK_E_ARG, "tensor %d: MXFP4 scales are required (4-byte aligned)", i);
   }
   HIP_TRY(hipSetDevice(c->device));
+  // FP8 re-encodings count their inexact elements in a device word of the workspace's status block
+  uint32_t *inexact = reinterpret_cast<uint32_t *>(c->scratch + c->o_status + 64);
+  bool reencoded = false;
+  std::vector<uint8_t *> reencoded_flags;
   for (int i = 0; i < n; ++i) {
     Slot *slot;
     int64_t ro, rows, cols;
@@ -1110,7 +1135,24 @@ mk_status mk_load_weights(mk_ctx *c, const mk_weight_desc *w, int n, void *strea
     Target tg;
     resolve(c, w[i], &slot, &ro, &rows, &cols, &have, &tg);
     if (tg.off >= 0) {  // expert matrix
-      if (tg.fmt == FMT_NVFP4) {
+      if (tg.fmt == FMT_FP8R || tg.fmt == FMT_MXFP4) {
+        if (tg.fmt == FMT_FP8R) {
+          if (!reencoded) HIP_TRY(hipMemsetAsync(inexact, 0, 4, st));
+          reencoded = true;
+          const int64_t total = rows * (cols / 256);
+          const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+          hipLaunchKernelGGL(mk_reencode_fp8, dim3(blocks), dim3(256), 0, st, static_cast<const uint8_t *>(w[i].data),
+                             static_cast<const uint8_t *>(w[i].scales), rows, cols, c->wbuf + tg.off, ro, tg.mrows, inexact);
+          reencoded_flags.push_back(tg.have_flag);
+        } else {
+          const int64_t total = (rows / 16) * (cols / 128) * 64;
+          const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+          hipLaunchKernelGGL(mk_repack_mxfp4, dim3(blocks), dim3(256), 0, st, static_cast<const uint8_t *>(w[i].data),
+                             static_cast<const uint8_t *>(w[i].scales), rows, cols, c->wbuf + tg.off, ro, tg.mrows);
+        }
+        HIP_TRY(hipGetLastError());
+        hipLaunchKernelGGL(mk_store_f32, dim3(1), dim3(1), 0, st, reinterpret_cast<float *>(c->wbuf + tg.ts_off), 1.0f);
+      } else if (tg.fmt == FMT_NVFP4) {
         const int64_t total = (rows / 16) * (cols / 128) * 64;
         const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
         hipLaunchKernelGGL(mk_repack_nvfp4, dim3(blocks), dim3(256), 0, st, static_cast<const uint8_t *>(w[i].data),
@@ -1148,6 +1190,16 @@ mk_status mk_load_weights(mk_ctx *c, const mk_weight_desc *w, int n, void *strea
       HIP_TRY(hipGetLastError());
     }
     *have |= kind_bit(w[i].kind);
+  }
+  if (reencoded) {  // the loader's bit-for-bit check of the FP8 re-encodings: wait for it, refuse on failure
+    uint32_t bad = 0;
+    HIP_TRY(hipMemcpyAsync(&bad, inexact, 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    if (bad) {
+      for (uint8_t *flag : reencoded_flags) *flag = 0;  // those matrices count as not loaded
+      return fail(MK_E_INEXACT, "FP8 re-encoding of MXFP4 gate/up weights is not lossless: %u elements have no exact "
+                                "E4M3 value at their block's bf16 scale", bad);
+    }
   }
   return MK_OK;
 }

@@ -11,7 +11,7 @@ constexpr int kWavesTotal = kCWaves + 1;
 constexpr int kThreads = kWavesTotal * 64;  // threads per workgroup
 constexpr int kCThreads = kCWaves * 64;     // threads of the compute waves
 constexpr int kRing = 12;                 // weight items in flight per compute wave (12 KiB), bf16 build
-constexpr int kRingNvfp4 = 10;            // the same for the build that also streams NVFP4 items
+constexpr int kRingNvfp4 = 8;            // the same for the build that also streams NVFP4 items
 constexpr int kRingWide = 10;             // the same for the build for more than 8 rows
 constexpr int kTileRows = 16;             // weight rows per MFMA tile
 constexpr int kFragK = 32;                // reduction columns per 1 KiB weight fragment
@@ -58,8 +58,12 @@ enum ActKind : int32_t {
 
 enum WeightFmt : int32_t {
   FMT_BF16 = 0,   // [tile][fragment][lane][8] bf16
-  FMT_NVFP4 = 1   // codes [tile][4-fragment group][lane][16 B], then scales [tile][group][32][4 B]
+  FMT_NVFP4 = 1,  // codes [tile][4-fragment group][lane][16 B], then E4M3 scales [tile][group][32][4 B]
+  FMT_FP8R = 2,   // FP8 E4M3 [tile][2-fragment item][lane][16 B], then bf16 scales [tile][256 columns][16]
+  FMT_MXFP4 = 3   // codes as NVFP4, then E8M0 scales [tile][group][16][4 B]
 };
+// MFMA fragments (16 rows x 32 columns) per 1 KiB stream item of a format
+constexpr int frags_per_item(int fmt) { return fmt == FMT_BF16 ? 1 : (fmt == FMT_FP8R ? 2 : 4); }
 
 enum OutKind : int32_t {
   OUT_PART = 0,   // partial sums per k-split -> part[dst]

@@ -20,10 +20,10 @@ MK_MAX_BATCH = 16
 MK_VERIFY_ROWS = 8
 
 STATUS = {0: "MK_OK", 1: "MK_E_ARG", 2: "MK_E_SHAPE", 3: "MK_E_UNSUPPORTED", 4: "MK_E_CAPACITY", 5: "MK_E_HIP",
-          6: "MK_E_DEVICE_TIMEOUT", 7: "MK_E_STATE"}
+          6: "MK_E_DEVICE_TIMEOUT", 7: "MK_E_STATE", 8: "MK_E_INEXACT"}
 MIXER = {"gqa": 0, "gdn": 1, "kda": 2, "mla": 3}
 FFN = {"dense": 0, "moe": 1}
-DTYPE = {"bf16": 0, "nvfp4": 1}
+DTYPE = {"bf16": 0, "nvfp4": 1, "mxfp4": 2}
 (W_EMBED, W_FINAL_NORM, W_LM_HEAD, W_ATTN_NORM, W_FFN_NORM, W_Q, W_K, W_V, W_A, W_B, W_O, W_DKV, W_KR, W_UK, W_UV,
  W_GATE, W_UP, W_DOWN, W_ROUTER) = range(19)
 _KIND_BY_SUFFIX = {"attn_norm": W_ATTN_NORM, "ffn_norm": W_FFN_NORM, "wq": W_Q, "wk": W_K, "wv": W_V, "wa": W_A,
@@ -223,12 +223,14 @@ class Megakernel:
             layer, kind, expert = weight_target(name)
             d = WeightDesc()
             d.layer, d.kind, d.expert = layer, kind, expert
-            if hasattr(a, "codes"):  # NVFP4: codes, E4M3 scales, tensor scale
+            if hasattr(a, "codes"):  # NVFP4 (codes, E4M3 scales, tensor scale) or MXFP4 (codes, E8M0 scales)
                 codes = torch.from_numpy(np.ascontiguousarray(a.codes)).to(self.device)
                 scales = torch.from_numpy(np.ascontiguousarray(a.scales)).to(self.device)
-                d.dtype = DTYPE["nvfp4"]
+                mx = getattr(a, "format", None) == "mxfp4"
+                d.dtype = DTYPE["mxfp4" if mx else "nvfp4"]
                 d.rows, d.cols = a.shape
-                d.data, d.scales, d.tensor_scale = codes.data_ptr(), scales.data_ptr(), float(a.tensor_scale)
+                d.data, d.scales = codes.data_ptr(), scales.data_ptr()
+                d.tensor_scale = 1.0 if mx else float(a.tensor_scale)
                 pending.append((d, (codes, scales)))
                 pend_bytes += codes.numel() + scales.numel()
             else:

@@ -179,7 +179,7 @@ class FullSizeWeights:
         if prefix != self.layer:
             self.layer, self.cache = prefix, {}
             print(f"  oracle {self.cfg.name}: {prefix}", flush=True)
-        if spec.kind == "nvfp4":
+        if spec.kind in ("nvfp4", "mxfp4"):
             key, src = bench.pooled_source(self.cfg, spec, self.expert_pool)
             if key not in self.pool:
                 self.pool[key] = self.synth.generate(src, self.cfg.seed)

@@ -155,3 +155,18 @@ def test_mla_schedule(mkmod, synth):
     n_chunks, chunk = att[12], att[13]
     assert chunk % 64 == 0 and n_chunks * chunk >= cfg.max_ctx > (n_chunks - 1) * chunk
     assert 8 * n_chunks * (hq // 8) <= h.sizes.n_workgroups
+
+
+def test_mx_expert_configs_schedule(mkmod, synth):
+    """MXFP4-shipped experts: the schedules build at both sizes, and the packed expert bytes follow the
+    formats (gate|up: one byte per weight plus a bf16 per 256; down: half a byte plus one per 32)."""
+    for name in ("c3ms", "c3m"):
+        cfg = synth.CONFIGS[name]
+        h = mkmod.HostContext(cfg, max_batch=8)
+        bf = mkmod.HostContext(synth.CONFIGS[name.replace("m", "", 1) if name == "c3m" else "c3s"], max_batch=8)
+        E = (cfg.n_experts + cfg.n_shared) * cfg.n_layers
+        F, Hd = cfg.expert_ffn, cfg.hidden
+        per_mx = 2 * F * Hd * (1 + 2 / 256) + F * Hd * (0.5 + 1 / 32)
+        per_bf = 3 * F * Hd * 2
+        diff = bf.sizes.packed_weights - h.sizes.packed_weights
+        assert abs(diff - E * (per_bf - per_mx)) <= E * 3 * 256 + 4096, (name, diff, E * (per_bf - per_mx))

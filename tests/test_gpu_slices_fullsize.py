@@ -71,7 +71,7 @@ def test_full_slice_properties(torch_gpu, synth, name, batch):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,batch", [("c3", 8), ("c4", 1), ("c4", 8)])
+@pytest.mark.parametrize("name,batch", [("c3", 8), ("c4", 1), ("c4", 8), ("c3m", 8)])
 def test_full_slice_matches_oracle(torch_gpu, oracle, synth, name, batch):
     """The same full-size slices against the oracle: the oracle reads the weights the benchmark loads
     (bench.build_gpu's seeded bf16 tensors and NVFP4 pool) one layer at a time, so it only ever holds
