@@ -335,6 +335,8 @@ struct Stream {
   int route_q;             // routing this workgroup holds (phase index of its expert gate/up product)
   int blocked;             // expert phase the stream waits at until the routing is known (-1: none)
   int fmt;                 // WeightFmt of the current phase
+  int scaled;              // the items carry a scale load (every format but bf16)
+  int sidx;                // this lane's word in an item's scale record (per lane)
   int kpos, kpos0;         // FP8: item index along the tile's row (current, first of the run)
   int tile_words;          // FP8: scale words per tile
   const uint32_t *sbase;   // FP8: the current tile's scales
@@ -380,6 +382,7 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
   st.sptr = reinterpret_cast<const uint32_t *>(a.wbuf);
   st.sstep = 0;
   st.fmt = FMT_BF16;  // no scale loads while the stream is done or blocked
+  st.scaled = 0;
   while (q >= 0 && q < a.phase_end) {
     CPhase *ph = cphase(a, q);
     if (ph->type == PH_GEMV) {
@@ -399,7 +402,13 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
         st.j = 0;
         st.skip = ph->KF / fpi - st.nfw;
         st.fmt = ph->fmt;
+        st.scaled = ph->fmt != FMT_BF16;
         st.sstep = ph->fmt == FMT_NVFP4 ? 32 : (ph->fmt == FMT_MXFP4 ? 16 : 0);
+        {  // the scale word of this lane's row: NVFP4 per half of the lane groups, MXFP4 one per row, FP8
+           // two rows' bf16 per word
+          const int ln = (int)threadIdx.x & 63;
+          st.sidx = ph->fmt == FMT_NVFP4 ? (ln & 15) + 16 * (ln >> 5) : (ph->fmt == FMT_MXFP4 ? ln & 15 : (ln & 15) >> 1);
+        }
         const int sT = ph->seg == SEG_EXPERT ? ph->seg_T : 0x40000000;
         st.seg = ph->seg == SEG_EXPERT ? u0 / sT : 0;
         int t = ph->seg == SEG_EXPERT ? u0 - st.seg * sT : u0;
@@ -424,24 +433,16 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
 __device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *smem, int wave, int lane,
                                             uint4 &v, uint32_t &sv) {
   v = ld_nt(st.ptr + lane);
-  if (st.fmt != FMT_BF16) {
-    // the scale word of this lane's row: NVFP4 per half of the lane groups, MXFP4 one per row, FP8 two
-    // rows' bf16 per word
-    const int sidx = st.fmt == FMT_NVFP4 ? (lane & 15) + 16 * (lane >> 5) : (st.fmt == FMT_MXFP4 ? lane & 15 : (lane & 15) >> 1);
-    sv = __builtin_nontemporal_load(st.sptr + sidx);
-  }
+  if (st.scaled) sv = __builtin_nontemporal_load(st.sptr + st.sidx);
   if (st.q >= 0) {
     st.ptr += 64;
-    if (st.fmt == FMT_FP8R) {
-      if ((++st.kpos & 3) == 0) st.sptr += 8;  // the next 256-column block
-    } else {
-      st.sptr += st.sstep;
-    }
-    if (++st.j == st.nfw) {
+    st.sptr += st.sstep;
+    if (__builtin_expect(st.fmt == FMT_FP8R, 0) && (++st.kpos & 3) == 0) st.sptr += 8;  // FP8: next 256-column block
+    if (__builtin_expect(++st.j == st.nfw, 0)) {  // end of a run: rare next to the items (laid out away from them)
       st.j = 0;
-      if (--st.left == 0) {
+      if (__builtin_expect(--st.left == 0, 0)) {
         stream_seek(st, a, smem, wave, cphase(a, st.q)->next_gemv);
-      } else if (--st.seg_left == 0) {  // next expert block, or the wrap of a rotated range
+      } else if (__builtin_expect(--st.seg_left == 0, 0)) {  // next expert block, or the wrap of a rotated range
         CPhase *ph = cphase(a, st.q);
         const int per = (int)gridDim.x / ph->S;
         const int s = (int)blockIdx.x / per;
@@ -809,7 +810,7 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
       }
     }
     stream_take(st, a, smem, wave, lane, r, sc);  // the slot's old item is consumed: refill it
-    if (++c_j == ipr) close_unit();
+    if (__builtin_expect(++c_j == ipr, 0)) close_unit();
   };
   // full turns of the ring: every slot consumed and refilled once per turn, so each item is waited
   // for with D - 1 younger items still in flight
