@@ -428,10 +428,22 @@ def cpu_baseline(cfg_full, layers=4, repeats=3):
                                         f"({per1:.2f} s per token)"}}
 
 
+KERNEL_SOURCES = ("mk_device.h", "mk_step.hip", "mk_step_nvfp4.hip", "mk_step_wide.hip", "mk_host.cpp", "mk_internal.h")
+
+
+def kernel_source_sha256():
+    """Hash of the sources the step kernels are built from (a counter profile holds for exactly these)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "persistent_megakernel_mk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
 def counter_traffic():
     """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by
     the calibration factors it records), or None when the kernel sources have changed since it was taken."""
-    import hashlib
     import re
 
     path = os.path.join(ROOT, "profiles", "mk_step_kernel_c1_b1.md")
@@ -441,10 +453,7 @@ def counter_traffic():
     if not m:
         return None
     info = json.loads(m.group(1))
-    h = hashlib.sha256()
-    for f in ("mk_device.h", "mk_step.hip", "mk_step_nvfp4.hip", "mk_host.cpp", "mk_internal.h"):
-        h.update(open(os.path.join(ROOT, "persistent_megakernel_mk_amd", "csrc", f), "rb").read())
-    if h.hexdigest() != info.get("kernel_source_sha256"):
+    if kernel_source_sha256() != info.get("kernel_source_sha256"):
         return None
     return info["traffic_bytes_per_launch"]
 
