@@ -149,7 +149,7 @@ def test_verify_with_all_drafts_accepted(torch_gpu, oracle, synth):
 
 def test_persistent_and_per_op_steps_interleave_on_one_context(torch_gpu, oracle, synth):
     """Steps 0 and 2 persistent, step 1 one launch per phase, on one context: the barrier counters and
-    their epoch carry over, so every step equals the all-persistent sequence on a second context bit for
+    the count of barriers already passed carry over, so every step equals the all-persistent sequence on a second context bit for
     bit and tracks the oracle."""
     cfg = synth.CONFIGS["c1s"].with_batch(2)
     W = synth.LazyWeights(cfg)
