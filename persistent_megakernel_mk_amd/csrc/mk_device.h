@@ -103,10 +103,24 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// v from the lane CTRL (a DPP lane pattern) names, within its 16-lane row
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// sum over the wave, the same value in every lane: DPP exchanges inside each 16-lane row (lane i ^ 1,
+// i ^ 2, then the mirrored lane of the 8-lane half and of the row: each step adds two equal-sized
+// partial sums, so all lanes of a row hold the same row sum), then the four row sums read from lanes
+// 0, 16, 32 and 48. No LDS round trips on this chain (a butterfly of lane shuffles takes six).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  const int b = __float_as_int(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0)), r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32)), r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -994,10 +1008,11 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
 // a the decay of each channel, S_r <- a * S_r; u = S_r . k; S_r <- S_r + beta (v_r - u) k; o_r = S_r . q.
 // A verify block advances each state row through its 8 token rows in order and records every
 // intermediate row (the snapshots the commit selects from).
-constexpr int kDeltaMaxRpw = 4;  // state rows per compute wave and unit
+constexpr int kDeltaMaxRpw = 16;  // state rows per compute wave and unit (units of up to 64 rows)
+template <bool SYNCW>  // SYNCW: the sync wave's copy (it forms gates only; no state rows)
 __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, Hl = a.lin_heads, dk = a.dk, dv = a.dv;
-  const int RPU = ph.chunk, RPW = RPU / kCWaves;  // state rows per unit / per compute wave
+  const int RPU = a.verify ? ph.chunk_verify : ph.chunk, RPW = RPU / kCWaves;  // state rows per unit / wave
   const int RB = dv / RPU;
   const int nseq = a.verify ? 1 : R;
   const int nj = a.verify ? R : 1;  // token rows applied to each state row, in order
@@ -1014,18 +1029,12 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
   const int c0 = lane * 2;
   for (int u = u0; u < u1; ++u) {
     const int b = u / (Hl * RB), h = (u / RB) % Hl, rb = u % RB;
-    // this wave's state rows start loading before the gates are formed
+    // this wave's state rows (all of them at once) start loading before the gates are formed
     float2 S[kDeltaMaxRpw];
-    float *Srow[kDeltaMaxRpw];
+    float *Sw = reinterpret_cast<float *>(a.ls[ph.layer]) + (((size_t)b * Hl + h) * dv + rb * RPU + wave * RPW) * dk + c0;
 #pragma unroll
-    for (int i = 0; i < kDeltaMaxRpw; ++i) {
-      Srow[i] = nullptr;
-      if (wave < kCWaves && i < RPW) {
-        const int r = rb * RPU + wave * RPW + i;
-        Srow[i] = reinterpret_cast<float *>(a.ls[ph.layer]) + (((size_t)b * Hl + h) * dv + r) * dk;
-        S[i] = *reinterpret_cast<const float2 *>(Srow[i] + c0);
-      }
-    }
+    for (int i = 0; i < kDeltaMaxRpw; ++i)
+      if (!SYNCW && wave < kCWaves && i < RPW) S[i] = *reinterpret_cast<const float2 *>(Sw + (size_t)i * dk);
     // gates and vectors: task t = (token row j, kind) for kinds q, k, decay + strength + values
     for (int t = wave; t < 3 * nj; t += kWavesTotal) {
       const int j = t / 3, kind = t - j * 3;
@@ -1064,10 +1073,10 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
       }
     }
     lds_barrier();
-    if (wave < kCWaves) {
+    if (!SYNCW && wave < kCWaves) {
 #pragma unroll
       for (int i = 0; i < kDeltaMaxRpw; ++i) {
-        if (i >= RPW) break;
+        if (i >= RPW) continue;  // (no break: the loop unrolls fully and S stays in registers)
         const int rl = wave * RPW + i, r = rb * RPU + rl;
         float2 st = S[i];
         for (int j = 0; j < nj; ++j) {
@@ -1089,7 +1098,7 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
             st_c(sn + 1, st.y);
           }
         }
-        if (!a.verify) *reinterpret_cast<float2 *>(Srow[i] + c0) = st;
+        if (!a.verify) *reinterpret_cast<float2 *>(Sw + (size_t)i * dk) = st;
       }
     }
     lds_barrier();  // LDS gates are reused by the next unit
@@ -1128,7 +1137,7 @@ struct GqaLds {
   static constexpr int st = p + 2 * 4 * 16 * 16;            // m, l, alpha [8]
 };
 
-template <int HD>
+template <int HD, bool SYNCW>  // SYNCW: the sync wave's copy (it stages K/V rows only)
 __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem) {
   typedef GqaLds<HD> L;
   const int R = a.R, nq = a.nq, nkv = a.nkv, grp = nq / nkv;
@@ -1158,7 +1167,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
     const size_t cbase = ((size_t)seq * nkv + g) * a.max_ctx;
     lds_barrier();  // the previous unit's LDS reads are done
     // queries of the group (rotated at prow) as the B operand
-    for (int it = tid; it < 8 * (HD / 8); it += kThreads) {
+    for (int it = SYNCW ? 8 * (HD / 8) : tid; it < 8 * (HD / 8); it += kCWaves * 64) {
       const int hl = it / (HD / 8), d0 = (it - hl * (HD / 8)) * 8;
       float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (hl < grp) {
@@ -1179,7 +1188,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
       Qb[(ks * 4 + kk) * 16 + hl] = pack_hi_lo(y, false);
       Qb[(ks * 4 + kk) * 16 + hl + 8] = pack_hi_lo(y, true);
     }
-    if (tid < 8) { mst[tid] = -INFINITY; lst[tid] = 0.0f; }
+    if (!SYNCW && tid < 8) { mst[tid] = -INFINITY; lst[tid] = 0.0f; }
     f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     for (int jb = j0; jb < j1; jb += kGqaSub) {
       lds_barrier();
@@ -1218,7 +1227,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
         *reinterpret_cast<uint4 *>(Vs + jj * L::rowb + d0 * 2) = vv;
       }
       lds_barrier();
-      if (wave < kCWaves) {  // scores: wave w takes positions jb + 16 w .. +15
+      if (!SYNCW && wave < kCWaves) {  // scores: wave w takes positions jb + 16 w .. +15
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -1235,7 +1244,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
         }
       }
       lds_barrier();
-      if (tid < 8 * 16) {  // online softmax: 16 lanes per query, 4 positions each
+      if (!SYNCW && tid < 8 * 16) {  // online softmax: 16 lanes per query, 4 positions each
         const int h = tid >> 4, q = tid & 15;
         float sv[4], bm = -INFINITY;
 #pragma unroll
@@ -1269,7 +1278,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
         }
       }
       lds_barrier();
-      if (wave < kCWaves) {  // out^T += V^T P: wave w takes dims w * HD/4 .. (HD/64 row blocks)
+      if (!SYNCW && wave < kCWaves) {  // out^T += V^T P: wave w takes dims w * HD/4 .. (HD/64 row blocks)
         const float al = alp[col & 7];
 #pragma unroll
         for (int rb = 0; rb < HD / 64; ++rb)
@@ -1296,7 +1305,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
     }
     lds_barrier();  // final statistics visible
     const int W = HD + 2;
-    if (wave < kCWaves) {
+    if (!SYNCW && wave < kCWaves) {
 #pragma unroll
       for (int rb = 0; rb < HD / 64; ++rb)
 #pragma unroll
@@ -1308,7 +1317,7 @@ __device__ __forceinline__ void attn_phase(CArgs &a, const Phase &ph, char *smem
           }
         }
     }
-    if (tid < grp) {
+    if (!SYNCW && tid < grp) {
       float *dst = a.attn + (((size_t)row * nq + g * grp + tid) * NC + c) * W;
       st_c(dst, mst[tid]);
       st_c(dst + 1, lst[tid]);
@@ -1697,13 +1706,14 @@ __device__ __forceinline__ void hidden_out_phase(CArgs &a) {
 using namespace mk;
 
 // Phases that every wave runs the same way; their results are acknowledged before the grid barrier.
+template <bool SYNCW>  // SYNCW: the sync wave's copy of the phase loop
 __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *smem) {
   switch (ph.type) {
     case PH_EMBED: embed_phase(a, ph, smem); break;
-    case PH_DELTA: delta_phase(a, ph, smem); break;
+    case PH_DELTA: delta_phase<SYNCW>(a, ph, smem); break;
     case PH_ATTN:
-      if (a.hd == 64) attn_phase<64>(a, ph, smem);
-      else attn_phase<128>(a, ph, smem);
+      if (a.hd == 64) attn_phase<64, SYNCW>(a, ph, smem);
+      else attn_phase<128, SYNCW>(a, ph, smem);
       break;
     case PH_MERGE:
     case PH_MLA_MERGE: merge_phase(a, ph, smem); break;
@@ -1743,7 +1753,7 @@ __device__ __forceinline__ void step_body(char *smem) {
         }
         gemv_sync<WIDE>(a, ph, smem);
       } else {
-        common_phase(a, ph, smem);
+        common_phase<true>(a, ph, smem);
       }
       __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are acknowledged before the barrier
       if (lane == 0) {
@@ -1787,7 +1797,7 @@ __device__ __forceinline__ void step_body(char *smem) {
         }
         gemv_compute<HAS_FP4, RING, WIDE>(a, ph, smem, ring, sring, st, head);
       } else {
-        common_phase(a, ph, smem);
+        common_phase<false>(a, ph, smem);
       }
       lds_barrier();
       if (abort_flag) return;

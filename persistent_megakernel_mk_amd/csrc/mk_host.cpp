@@ -421,8 +421,17 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       mx.type = PH_DELTA;
       mx.lin_idx = c->lin_index[l];
       mx.per_channel_gate = m == MK_MIXER_KDA;
-      // state rows per unit: 8 while that gives at most one unit per workgroup, else 16
-      mx.chunk = (int64_t)(R) * f.lin_heads * (f.d_v / 8) <= G ? 8 : 16;
+      // state rows per unit: the fewest (8, 16, 32, 64) that give at most one unit per workgroup, else
+      // 64: a workgroup's units run one after another, each a round trip to memory, while the rows of
+      // one unit load together. A verify block (one sequence, 8 token rows applied in order) counts
+      // its units separately.
+      auto rows_per_unit = [&](int64_t seqs) {
+        int rpu = 8;
+        while (rpu < 64 && rpu < f.d_v && seqs * f.lin_heads * (f.d_v / rpu) > G) rpu *= 2;
+        return rpu;
+      };
+      mx.chunk = rows_per_unit(R);
+      mx.chunk_verify = rows_per_unit(1);
       sc.phases.push_back(mx);
     }
     if (m != MK_MIXER_MLA) {

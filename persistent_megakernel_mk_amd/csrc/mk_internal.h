@@ -110,6 +110,7 @@ struct Phase {
   int32_t heads, hgroup;                // query heads, heads per unit
   int32_t mla_src;                      // partial buffer of the absorbed queries
   int32_t step;       // decode step of a multi-step launch this phase belongs to (0 in a one-step table)
+  int32_t chunk_verify;  // delta rule: state rows per unit in a verify block (chunk: in a decode step)
 };
 
 struct StepArgs {

@@ -170,3 +170,20 @@ def test_mx_expert_configs_schedule(mkmod, synth):
         per_bf = 3 * F * Hd * 2
         diff = bf.sizes.packed_weights - h.sizes.packed_weights
         assert abs(diff - E * (per_bf - per_mx)) <= E * 3 * 256 + 4096, (name, diff, E * (per_bf - per_mx))
+
+
+def test_delta_rule_units(mkmod, synth):
+    """Gated delta rule: each unit is a block of one head's state rows; the block is the smallest of
+    8, 16, 32 and 64 rows that leaves at most one unit per workgroup (a workgroup's units run one after
+    another), else 64."""
+    G = 256
+    for name, rows, want in (("c1", 1, 8), ("c1", 4, 32), ("c1", 8, 64), ("c3", 8, 64)):
+        cfg = synth.CONFIGS[name]
+        h = mkmod.HostContext(cfg, max_batch=8)
+        assert h.sizes.n_workgroups == G
+        delta = [p for p in h.phases(rows) if p[0] == 3]
+        assert len(delta) == sum(m in ("gdn", "kda") for m in cfg.mixers)
+        for p in delta:
+            assert p[13] == want, (name, rows, p[13])
+            units = rows * cfg.lin_heads * (cfg.d_v // p[13])
+            assert units <= G or p[13] == 64
