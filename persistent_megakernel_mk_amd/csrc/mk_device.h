@@ -349,7 +349,6 @@ struct Stream {
   int route_q;             // routing this workgroup holds (phase index of its expert gate/up product)
   int blocked;             // expert phase the stream waits at until the routing is known (-1: none)
   int fmt;                 // WeightFmt of the current phase
-  int scaled;              // the items carry a scale load (every format but bf16)
   int sidx;                // this lane's word in an item's scale record (per lane)
   int kpos, kpos0;         // FP8: item index along the tile's row (current, first of the run)
   int tile_words;          // FP8: scale words per tile
@@ -393,10 +392,10 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
   st.left = 0;
   st.blocked = -1;
   st.ptr = reinterpret_cast<const uint4 *>(a.wbuf);
-  st.sptr = reinterpret_cast<const uint32_t *>(a.wbuf);
-  st.sstep = 0;
-  st.fmt = FMT_BF16;  // no scale loads while the stream is done or blocked
-  st.scaled = 0;
+  st.sptr = reinterpret_cast<const uint32_t *>(a.wbuf);  // scale loads of a done or blocked stream: a fixed
+  st.sstep = 0;                                          // word of the weight buffer
+  st.sidx = 0;
+  st.fmt = FMT_BF16;
   while (q >= 0 && q < a.phase_end) {
     CPhase *ph = cphase(a, q);
     if (ph->type == PH_GEMV) {
@@ -416,7 +415,6 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
         st.j = 0;
         st.skip = ph->KF / fpi - st.nfw;
         st.fmt = ph->fmt;
-        st.scaled = ph->fmt != FMT_BF16;
         st.sstep = ph->fmt == FMT_NVFP4 ? 32 : (ph->fmt == FMT_MXFP4 ? 16 : 0);
         {  // the scale word of this lane's row: NVFP4 per half of the lane groups, MXFP4 one per row, FP8
            // two rows' bf16 per word
@@ -442,12 +440,16 @@ __device__ __forceinline__ void stream_seek(Stream &st, CArgs &a, const char *sm
   }
 }
 
-// Always issues both loads (dummies once the stream is done), so a ring slot is only ever written by
-// a load and its register never needs a copy that would wait for the load.
+// Always issues its loads (dummies once the stream is done), so a ring slot is only ever written by a
+// load and its register never needs a copy that would wait for the load. The build that decodes
+// narrow formats loads a scale word with every item (for a bf16 item, one fixed word of the weight
+// buffer), so every slot issues the same two loads and each slot's wait leaves the younger slots'
+// loads in flight.
+template <bool HAS_FP4>
 __device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *smem, int wave, int lane,
                                             uint4 &v, uint32_t &sv) {
   v = ld_nt(st.ptr + lane);
-  if (st.scaled) sv = __builtin_nontemporal_load(st.sptr + st.sidx);
+  if (HAS_FP4) sv = __builtin_nontemporal_load(st.sptr + st.sidx);
   if (st.q >= 0) {
     st.ptr += 64;
     st.sptr += st.sstep;
@@ -514,6 +516,24 @@ __device__ __forceinline__ void lds_wait_ge(uint32_t *p, uint32_t v, CArgs &a) {
       st_ci(a.status + 0, 6 /* MK_E_DEVICE_TIMEOUT */);
       st_ci(a.status + 2, 1);
       return;
+    }
+  }
+}
+
+// Bounded wait until a finaliser counter (written by other workgroups) reaches v; the abort flag is
+// polled too. On expiry the step is marked timed out; false on expiry or abort.
+__device__ __forceinline__ bool fin_wait(CArgs &a, const uint32_t *cnt, uint32_t v) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (uint32_t it = 0;; ++it) {
+    const uint32_t c = ld_cu(cnt);
+    const int32_t ab = (it & 15u) == 15u ? ld_ci(a.status + 2) : 0;
+    if (c >= v) return true;
+    if (ab != 0) return false;
+    __builtin_amdgcn_s_sleep(1);
+    if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > a.timeout_ticks) {
+      st_ci(a.status + 0, 6 /* MK_E_DEVICE_TIMEOUT */);
+      st_ci(a.status + 2, 1);
+      return false;
     }
   }
 }
@@ -706,16 +726,25 @@ __device__ __forceinline__ bf16x8 nvfp4_frag(uint32_t codes, float scale) {
   return bf16x8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
 }
 
-// E8M0 scale byte -> fp32: 2^(e - 127) (e = 0 gives the subnormal 2^-127)
-__device__ __forceinline__ float e8m0_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
+// The scaled conversions below (v_cvt_scalef32_pk_bf16_*) multiply by two to the power of the scale
+// operand's exponent field only, so they take power-of-two scales: an E8M0 byte e is passed as the
+// float whose exponent field is e. Each conversion gives two bf16 weights, exact (an E2M1 value has two
+// significant bits, an E4M3 value four, and the scales keep the products in bf16's normal range).
+
+// Eight MXFP4 weights of one lane times their E8M0 block scale e -> bf16. Element 2i is the low nibble of
+// byte i.
+__device__ __forceinline__ bf16x8 mxfp4_frag(uint32_t codes, uint32_t e) {
+  const float sc = __uint_as_float(e << 23);
+  bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0), b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
+  bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2), b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
+  return bf16x8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+}
 
 // Eight FP8 E4M3 weights of one lane (bytes of lo, then hi) times their power-of-two bf16 block scale ->
-// bf16 (exact: an E4M3 value has four significant bits).
+// bf16.
 __device__ __forceinline__ bf16x8 fp8_frag(uint32_t lo, uint32_t hi, float scale) {
-  f32x2 p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false), p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-  f32x2 p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false), p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-  bf16x2 b0 = __builtin_convertvector(p0 * scale, bf16x2), b1 = __builtin_convertvector(p1 * scale, bf16x2);
-  bf16x2 b2 = __builtin_convertvector(p2 * scale, bf16x2), b3 = __builtin_convertvector(p3 * scale, bf16x2);
+  bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, false), b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, scale, true);
+  bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, false), b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, scale, true);
   return bf16x8{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
 }
 
@@ -784,32 +813,38 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
     if (FP8) {  // the lane's row scale: half (lane & 1) of the scale word
       const float s8 = __uint_as_float(((sc >> ((lane & 1) * 16)) & 0xFFFFu) << 16);
       const uint32_t cw[4] = {r.x, r.y, r.z, r.w};
+      uint4 bv[2];  // the item's two activation fragments: their LDS reads in flight together
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
-        uint4 bv = uint4{0u, 0u, 0u, 0u};
-        if (col < 2 * R) bv = aw[((c_j * 2 + f) * 4 + kgrp) * C + col];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_frag(cw[2 * f], cw[2 * f + 1], s8), __builtin_bit_cast(bf16x8, bv),
-                                                      acc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);  // one fragment's dequantised weights live at a time
+        bv[f] = uint4{0u, 0u, 0u, 0u};
+        if (col < 2 * R) bv[f] = aw[((c_j * 2 + f) * 4 + kgrp) * C + col];
       }
-    } else if (FP4) {
-      float sc4[4];
-      if (MX) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) sc4[f] = e8m0_f32((sc >> (8 * f)) & 255u);
-      } else {
+      for (int f = 0; f < 2; ++f)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8_frag(cw[2 * f], cw[2 * f + 1], s8), __builtin_bit_cast(bf16x8, bv[f]),
+                                                      acc, 0, 0, 0);
+    } else if (FP4) {
+      const uint32_t cw[4] = {r.x, r.y, r.z, r.w};
+      uint4 bv[4];  // the item's four activation fragments: their LDS reads in flight together
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        bv[f] = uint4{0u, 0u, 0u, 0u};
+        if (col < 2 * R) bv[f] = aw[((c_j * 4 + f) * 4 + kgrp) * C + col];
+      }
+      if (MX) {  // E8M0 scales: byte f of the scale word
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mxfp4_frag(cw[f], (sc >> (8 * f)) & 255u), __builtin_bit_cast(bf16x8, bv[f]),
+                                                        acc, 0, 0, 0);
+      } else {  // E4M3 scales (not powers of two): converted, then multiplied in fp32
+        float sc4[4];
         sc4[0] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 0);
         sc4[1] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 1);
         sc4[2] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 2);
         sc4[3] = __builtin_amdgcn_cvt_f32_fp8((int)sc, 3);
-      }
-      const uint32_t cw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        uint4 bv = uint4{0u, 0u, 0u, 0u};
-        if (col < 2 * R) bv = aw[((c_j * 4 + f) * 4 + kgrp) * C + col];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nvfp4_frag(cw[f], sc4[f]), __builtin_bit_cast(bf16x8, bv), acc, 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);  // one fragment's dequantised weights live at a time
+        for (int f = 0; f < 4; ++f)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nvfp4_frag(cw[f], sc4[f]), __builtin_bit_cast(bf16x8, bv[f]), acc, 0, 0, 0);
       }
     } else {
       uint4 bv = uint4{0u, 0u, 0u, 0u};
@@ -823,7 +858,7 @@ __device__ __forceinline__ void gemv_run(CArgs &a, const Phase &ph, char *smem, 
                                                        0, 0, 0);
       }
     }
-    stream_take(st, a, smem, wave, lane, r, sc);  // the slot's old item is consumed: refill it
+    stream_take<HAS_FP4>(st, a, smem, wave, lane, r, sc);  // the slot's old item is consumed: refill it
     if (__builtin_expect(++c_j == ipr, 0)) close_unit();
   };
   // full turns of the ring: every slot consumed and refilled once per turn, so each item is waited
@@ -905,6 +940,10 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   const int nrot = u1 - u0, r0 = rotated(ph) ? rot_start(s, ph.S, nrot) : 0;
   const bool fin = needs_finalise(ph);
   const bool direct_resid = ph.out == OUT_RESID && S_eff == 1;
+  // expert down products: a tile has one partial per (expert, k-split) and a workgroup many small
+  // units, so contributions are counted once after all of this workgroup's units, and each tile is
+  // finalised by one designated workgroup (tile t by workgroup t mod G) once its count is complete
+  const bool deferred = fin && expert && !direct_resid;
   for (int unit = 0; unit < nrot; ++unit) {
     const int u = u0 + (r0 + unit < nrot ? r0 + unit : r0 + unit - nrot);
     const int sl = unit % kRedSlots;
@@ -963,7 +1002,7 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
         st_c(a.ss + (size_t)lane * (a.H / kTileRows) + u, v);
       }
       wave_lds_sync();
-    } else if (fin) {
+    } else if (fin && !deferred) {
       // count this contribution as soon as its partials are acknowledged; the last contributor of the
       // tile finalises it right away (while the compute waves stream the remaining units) and resets
       // the tile's counter for the next step
@@ -976,6 +1015,17 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
         if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (__shfl(last, 0)) finalise_tiles<NK>(a, ph, tl, S_eff, TN, best_v[0], best_i[0]);
+    }
+  }
+  if (deferred) {
+    __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials are acknowledged: count them
+    for (int unit = lane; unit < nrot; unit += 64)
+      __hip_atomic_fetch_add(a.fin + ph.cnt_off + (u0 + unit) % ph.seg_T, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = blockIdx.x; t < ph.seg_T; t += gridDim.x) {
+      uint32_t *cnt = a.fin + ph.cnt_off + t;
+      if (!fin_wait(a, cnt, (uint32_t)S_eff)) break;
+      finalise_tiles<NK>(a, ph, t, S_eff, TN, best_v[0], best_i[0]);
+      if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next step
     }
   }
   if (ph.out == OUT_LOGITS) {  // per-workgroup argmax candidate of each row (first index on ties)
@@ -1778,7 +1828,7 @@ __device__ __forceinline__ void step_body(char *smem) {
       while (q < a.phase_end && cphase(a, q)->type != PH_GEMV) ++q;
       stream_seek(st, a, smem, wave, q < a.phase_end ? q : -1);
 #pragma unroll
-      for (int d = 0; d < RING; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
+      for (int d = 0; d < RING; ++d) stream_take<HAS_FP4>(st, a, smem, wave, lane, ring[d], sring[d]);
     }
     for (int p = ap->phase_begin; p < ap->phase_end; ++p) {
       CArgs &a = *ap;
@@ -1792,8 +1842,11 @@ __device__ __forceinline__ void step_body(char *smem) {
           st.route_q = route_q;
           stream_seek(st, a, smem, wave, p);
 #pragma unroll
-          for (int d = 0; d < RING; ++d) stream_take(st, a, smem, wave, lane, ring[d], sring[d]);
+          for (int d = 0; d < RING; ++d) stream_take<HAS_FP4>(st, a, smem, wave, lane, ring[d], sring[d]);
           head = 0;
+          // the refilled slots land before the ring loop: otherwise the compiler's wait counts for the
+          // loop (which joins this path) assume these loads may still be in flight and drain the ring
+          __builtin_amdgcn_s_waitcnt(0);
         }
         gemv_compute<HAS_FP4, RING, WIDE>(a, ph, smem, ring, sring, st, head);
       } else {
