@@ -563,50 +563,20 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
   const int j0 = first_piece_seg(ph, u0);
   const int np = shared_act(ph) ? 1 : (u1 - 1) / ph.seg_T - j0 + 1;
   const RouteLds *rt = route_lds(smem);
-  // each thread keeps one row b and walks the 8-column groups with a fixed stride (no divisions)
+  // each thread keeps one row b and walks the 8-column groups with a fixed stride; the loads of NB of
+  // its groups are issued together (addresses clamped to a valid group, so none is conditional), then
+  // the groups are converted and stored
   const int tpr = kThreads / R;  // threads per row
   const int b = (int)threadIdx.x % R, kg0 = (int)threadIdx.x / R;
   const int ngroups = (nk / 8) * np;
-  for (int gi = kg0; threadIdx.x < tpr * R && gi < ngroups; gi += tpr) {
-    int pc = 0, kg = gi;
+  const int C = act_stride<WIDE>(R);
+  const int grp = WIDE ? b >> 3 : 0, bl = WIDE ? b & 7 : b, Rg = WIDE ? min(8, R - 8 * grp) : R;
+  auto locate = [&](int gi, int &pc, int &kg) {  // group -> activation piece and 8-column group in it
+    pc = 0;
+    kg = gi;
     while (kg >= nk / 8) { kg -= nk / 8; ++pc; }
-    const int k = k0 + kg * 8;
-    const int j = j0 + pc;
-    const int off = ph.src_off + j * ph.src_seg + k;
-    float y[8];
-    if (ph.act == ACT_NORM) {
-      const float *xp = a.x + (size_t)b * a.H + k;
-      const float4 x0 = ld_c4(xp), x1 = ld_c4(xp + 4);
-      const uint16_t *gp = reinterpret_cast<const uint16_t *>(a.wbuf + ph.gain_off) + k;
-      uint4 gg = *reinterpret_cast<const uint4 *>(gp);
-      float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      uint32_t gw[4] = {gg.x, gg.y, gg.z, gg.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float g = bf2f((uint16_t)(gw[e >> 1] >> ((e & 1) * 16)));
-        y[e] = xs[e] * g;
-      }
-    } else if (ph.act == ACT_MIX) {
-      const float *mp = a.mix + (size_t)b * a.mix_stride + off;
-      const float4 m0 = ld_c4(mp), m1 = ld_c4(mp + 4);
-      y[0] = m0.x; y[1] = m0.y; y[2] = m0.z; y[3] = m0.w; y[4] = m1.x; y[5] = m1.y; y[6] = m1.z; y[7] = m1.w;
-    } else {
-      const float *src = part_of(a, ph.src_part);
-      float g[8] = {0, 0, 0, 0, 0, 0, 0, 0}, u[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int s2 = 0; s2 < ph.src_S; ++s2) {
-        const float *row = src + ((size_t)s2 * R + b) * ph.src_N + off;
-        const float4 p0 = ld_c4(row), p1 = ld_c4(row + 4);
-        g[0] += p0.x; g[1] += p0.y; g[2] += p0.z; g[3] += p0.w; g[4] += p1.x; g[5] += p1.y; g[6] += p1.z; g[7] += p1.w;
-        if (ph.act == ACT_SWIGLU) {
-          const float *up = row + ph.K;  // up rows follow the gate rows
-          const float4 q0 = ld_c4(up), q1 = ld_c4(up + 4);
-          u[0] += q0.x; u[1] += q0.y; u[2] += q0.z; u[3] += q0.w; u[4] += q1.x; u[5] += q1.y; u[6] += q1.z; u[7] += q1.w;
-        }
-      }
-      const float w = ph.seg == SEG_EXPERT ? rt->wt[j][b] : 1.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (ph.act == ACT_SWIGLU) ? silu(g[e]) * u[e] * w : g[e];
-    }
+  };
+  auto store = [&](const float (&y)[8], int pc, int kg) {
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -615,11 +585,90 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
       hi[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
       lo[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
-    const int f = kg >> 2, g4 = kg & 3, C = act_stride<WIDE>(R);
-    const int grp = WIDE ? b >> 3 : 0, bl = WIDE ? b & 7 : b, Rg = WIDE ? min(8, R - 8 * grp) : R;
+    const int f = kg >> 2, g4 = kg & 3;
     uint4 *pa = act + (size_t)pc * (nk / 8) * C + grp * 16;
     pa[(f * 4 + g4) * C + bl] = uint4{hi[0], hi[1], hi[2], hi[3]};
     pa[(f * 4 + g4) * C + Rg + bl] = uint4{lo[0], lo[1], lo[2], lo[3]};
+  };
+  if (threadIdx.x >= tpr * R) return;
+  if (ph.act == ACT_NORM || ph.act == ACT_MIX) {
+    constexpr int NB = 2;
+    for (int gb = kg0; gb < ngroups; gb += NB * tpr) {
+      float4 v0[NB], v1[NB];
+      uint4 gg[NB];
+      int pcs[NB], kgs[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        locate(min(gb + i * tpr, ngroups - 1), pcs[i], kgs[i]);
+        const int k = k0 + kgs[i] * 8;
+        if (ph.act == ACT_NORM) {
+          const float *xp = a.x + (size_t)b * a.H + k;
+          v0[i] = ld_c4(xp);
+          v1[i] = ld_c4(xp + 4);
+          gg[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(a.wbuf + ph.gain_off) + k);
+        } else {
+          const float *mp = a.mix + (size_t)b * a.mix_stride + ph.src_off + (j0 + pcs[i]) * ph.src_seg + k;
+          v0[i] = ld_c4(mp);
+          v1[i] = ld_c4(mp + 4);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (gb + i * tpr >= ngroups) continue;
+        float y[8] = {v0[i].x, v0[i].y, v0[i].z, v0[i].w, v1[i].x, v1[i].y, v1[i].z, v1[i].w};
+        if (ph.act == ACT_NORM) {
+          const uint32_t gw[4] = {gg[i].x, gg[i].y, gg[i].z, gg[i].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] *= bf2f((uint16_t)(gw[e >> 1] >> ((e & 1) * 16)));
+        }
+        store(y, pcs[i], kgs[i]);
+      }
+    }
+  } else {  // partial sums of an earlier product (k-splits summed), SwiGLU of gate and up rows
+    constexpr int NB = 1;  // (more would spill the compute waves, whose registers hold the weight ring)
+    const float *src = part_of(a, ph.src_part);
+    for (int gb = kg0; gb < ngroups; gb += NB * tpr) {
+      float g[NB][8], u[NB][8];
+      int pcs[NB], kgs[NB], offs[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        locate(min(gb + i * tpr, ngroups - 1), pcs[i], kgs[i]);
+        offs[i] = ph.src_off + (j0 + pcs[i]) * ph.src_seg + k0 + kgs[i] * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) g[i][e] = u[i][e] = 0.0f;
+      }
+      for (int s2 = 0; s2 < ph.src_S; ++s2) {
+        float4 p0[NB], p1[NB], q0[NB], q1[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const float *row = src + ((size_t)s2 * R + b) * ph.src_N + offs[i];
+          p0[i] = ld_c4(row);
+          p1[i] = ld_c4(row + 4);
+          if (ph.act == ACT_SWIGLU) {  // up rows follow the gate rows
+            q0[i] = ld_c4(row + ph.K);
+            q1[i] = ld_c4(row + ph.K + 4);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          g[i][0] += p0[i].x; g[i][1] += p0[i].y; g[i][2] += p0[i].z; g[i][3] += p0[i].w;
+          g[i][4] += p1[i].x; g[i][5] += p1[i].y; g[i][6] += p1[i].z; g[i][7] += p1[i].w;
+          if (ph.act == ACT_SWIGLU) {
+            u[i][0] += q0[i].x; u[i][1] += q0[i].y; u[i][2] += q0[i].z; u[i][3] += q0[i].w;
+            u[i][4] += q1[i].x; u[i][5] += q1[i].y; u[i][6] += q1[i].z; u[i][7] += q1[i].w;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        if (gb + i * tpr >= ngroups) continue;
+        const float w = ph.seg == SEG_EXPERT ? rt->wt[j0 + pcs[i]][b] : 1.0f;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (ph.act == ACT_SWIGLU) ? silu(g[i][e]) * u[i][e] * w : g[i][e];
+        store(y, pcs[i], kgs[i]);
+      }
+    }
   }
 }
 
