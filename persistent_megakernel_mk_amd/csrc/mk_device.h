@@ -127,6 +127,25 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 __device__ __forceinline__ float softplusf_(float a) { return a > 20.0f ? a : log1pf(__expf(a)); }
 
+// Writes activation value y of row b at column k into a staged buffer: the bf16 high half and the
+// bf16 low half (y minus the high half) at the B-operand positions the LDS copy of a product expects
+// ([k / 8][C][8]: up to 8 rows, columns b and R + b; above, row group b / 8 at columns 16 (b / 8) +
+// (b % 8) and 16 (b / 8) + rows-in-group + (b % 8)).
+__device__ __forceinline__ void stg_put(uint16_t *buf, int R, int k, int b, float y) {
+  const bool wide = R > kMaxRows;
+  const int C = wide ? 32 : 2 * R;
+  const int grp = wide ? b >> 3 : 0, bl = wide ? b & 7 : b, Rg = wide ? min(8, R - 8 * grp) : R;
+  const size_t u = (size_t)(k >> 3) * C + grp * 16 + bl;
+  const uint16_t hi = f2bf(y), lo = f2bf(y - bf2f(hi));
+  __hip_atomic_store(buf + u * 8 + (k & 7), hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // device-coherent
+  __hip_atomic_store(buf + (u + Rg) * 8 + (k & 7), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// x writers: x times the bf16 gain of the RMSNorm that reads it next, staged
+__device__ __forceinline__ void stg_put_x(CArgs &a, const Phase &ph, int n, int b, float v) {
+  const float g = bf2f(reinterpret_cast<const uint16_t *>(a.wbuf + ph.stg_gain_off)[n]);
+  stg_put(a.stg[0], a.R, n, b, v * g);
+}
+
 // ---------------------------------------------------------------------------------------------
 // grid barrier: two-level counters (8 groups, then one top counter), monotone across steps.
 // Run by lane 0 of the sync wave; the caller brackets it with workgroup barriers.
@@ -590,6 +609,21 @@ __device__ __forceinline__ void prep_act(CArgs &a, const Phase &ph, int s, int u
     pa[(f * 4 + g4) * C + bl] = uint4{hi[0], hi[1], hi[2], hi[3]};
     pa[(f * 4 + g4) * C + Rg + bl] = uint4{lo[0], lo[1], lo[2], lo[3]};
   };
+  if (ph.stg_in != STG_NONE && np == 1) {
+    // the producer wrote the fragments in this layout: copy the K slice into LDS, 1 KiB per wave and
+    // instruction (direct-to-LDS loads, device-coherent), and wait for the copies before the barrier
+    const int bytes = (nk / 8) * C * 16;
+    const char *src = reinterpret_cast<const char *>(a.stg[ph.stg_in - 1]) + (size_t)(k0 / 8) * C * 16;
+    const int w = (int)threadIdx.x >> 6, ln = (int)threadIdx.x & 63;
+    for (int c = w; c * 1024 < bytes; c += kWavesTotal) {
+      const int o = c * 1024 + ln * 16;
+      if (o < bytes)
+        __builtin_amdgcn_global_load_lds(src + o, (__attribute__((address_space(3))) void *)(reinterpret_cast<char *>(act) + c * 1024),
+                                         16, 0, 16 /* sc1: device-coherent */);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
   if (threadIdx.x >= tpr * R) return;
   if (ph.act == ACT_NORM || ph.act == ACT_MIX) {
     constexpr int NB = 2;
@@ -733,6 +767,7 @@ __device__ __forceinline__ void finalise_tiles(CArgs &a, const Phase &ph, int ti
       if (ok_k[k]) {
         v += xv[k];
         st_c(a.x + (size_t)b * a.H + n, v);
+        if (ph.stg_out) stg_put_x(a, ph, n, b, v);
       }
       float q2 = ok_k[k] ? v * v : 0.0f;  // sum of squares over the tile's 16 rows (16 consecutive lanes)
 #pragma unroll
@@ -939,6 +974,57 @@ __device__ __forceinline__ void gemv_compute(CArgs &a, const Phase &ph, char *sm
   gemv_run<HAS_FP4, D, WIDE>(a, ph, smem, ring, sring, st, head, s, u0, u1);
 }
 
+// Dense gate|up product whose SwiGLU is staged: the designated workgroup of a 16-row pair t (gate tile t
+// and up tile t + T/2, every k-split) sums the k-split partials in k-split order, as the product that
+// reads them would, and writes silu(gate) * up of the pair's 16 columns for each row.
+// Pairs t0, t0 + G, ... (up to kSwiBatch of them, all below Th) at once: every partial load in flight
+// together (two k-splits at a time), then the sums, SwiGLU and staged writes. Five pairs per batch up
+// to 8 rows, two above (the sync wave's registers).
+template <int NK>
+__device__ __forceinline__ void swiglu_pairs(CArgs &a, const Phase &ph, int t0, int n) {
+  constexpr int kSwiBatch = NK == 2 ? 5 : 2;
+  const int R = a.R, lane = threadIdx.x & 63, Th = ph.T / 2, G = gridDim.x;
+  const float *pp = part_of(a, ph.dst_part);
+  float g[kSwiBatch][NK], u[kSwiBatch][NK];
+#pragma unroll
+  for (int i = 0; i < kSwiBatch; ++i)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) g[i][k] = u[i][k] = 0.0f;
+  for (int s2 = 0; s2 < ph.S; s2 += 2) {
+    const bool two = s2 + 1 < ph.S;
+    float pg[kSwiBatch][NK][2], pu[kSwiBatch][NK][2];
+#pragma unroll
+    for (int i = 0; i < kSwiBatch; ++i)
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int idx = lane + 64 * k, row = idx & 15, b = idx < 16 * R ? idx >> 4 : 0;  // (a valid dummy)
+          const int t = t0 + (i < n ? i : 0) * G;
+          const float *pr = pp + ((size_t)(two ? s2 + h : s2) * R + b) * ph.N + row;
+          pg[i][k][h] = ld_c(pr + (size_t)t * kTileRows);
+          pu[i][k][h] = ld_c(pr + (size_t)(t + Th) * kTileRows);
+        }
+#pragma unroll
+    for (int i = 0; i < kSwiBatch; ++i)
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !two) continue;
+          g[i][k] += pg[i][k][h];
+          u[i][k] += pu[i][k][h];
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < kSwiBatch; ++i)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int idx = lane + 64 * k;
+      if (i < n && idx < 16 * R) stg_put(a.stg[2], R, (t0 + i * G) * kTileRows + (idx & 15), idx >> 4, silu(g[i][k]) * u[i][k]);
+    }
+}
+
 // sync wave: activation staging (with the compute waves), norm statistics, per-unit reduction and
 // stores, finalisation
 template <bool WIDE>
@@ -993,6 +1079,7 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   // units, so contributions are counted once after all of this workgroup's units, and each tile is
   // finalised by one designated workgroup (tile t by workgroup t mod G) once its count is complete
   const bool deferred = fin && expert && !direct_resid;
+  const bool swi = ph.out == OUT_PART && ph.stg_out;  // dense gate|up: SwiGLU of complete pairs, staged
   for (int unit = 0; unit < nrot; ++unit) {
     const int u = u0 + (r0 + unit < nrot ? r0 + unit : r0 + unit - nrot);
     const int sl = unit % kRedSlots;
@@ -1029,6 +1116,7 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
           const int n = u * kTileRows + row;
           const float xn = ld_c(a.x + (size_t)b * a.H + n) + v;
           st_c(a.x + (size_t)b * a.H + n, xn);
+          if (ph.stg_out) stg_put_x(a, ph, n, b, xn);
           xsq[k] = xn * xn;
         } else if (expert && ph.out == OUT_RESID) {
           st_c(part_of(a, ph.dst_part) + ((size_t)(j * ph.S + s) * R + b) * TN + tl * kTileRows + row, v);
@@ -1066,15 +1154,36 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
       if (__shfl(last, 0)) finalise_tiles<NK>(a, ph, tl, S_eff, TN, best_v[0], best_i[0]);
     }
   }
-  if (deferred) {
-    __builtin_amdgcn_s_waitcnt(0);  // this workgroup's partials are acknowledged: count them
-    for (int unit = lane; unit < nrot; unit += 64)
-      __hip_atomic_fetch_add(a.fin + ph.cnt_off + (u0 + unit) % ph.seg_T, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int t = blockIdx.x; t < ph.seg_T; t += gridDim.x) {
-      uint32_t *cnt = a.fin + ph.cnt_off + t;
-      if (!fin_wait(a, cnt, (uint32_t)S_eff)) break;
-      finalise_tiles<NK>(a, ph, t, S_eff, TN, best_v[0], best_i[0]);
-      if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next step
+  if (deferred || swi) {
+    // expert down tiles: one count per (segment, k-split); dense gate|up pairs: one per (gate or up
+    // tile, k-split). All of this workgroup's partials are acknowledged once, then counted; each tile
+    // or pair is finalised by its designated workgroup (index mod G) when its count is complete.
+    __builtin_amdgcn_s_waitcnt(0);
+    const int Th = ph.T / 2;
+    uint32_t *cnt0 = a.fin + (swi ? ph.swi_cnt_off : ph.cnt_off);
+    for (int unit = lane; unit < nrot; unit += 64) {
+      const int u = u0 + unit;
+      __hip_atomic_fetch_add(cnt0 + (swi ? (u < Th ? u : u - Th) : u % ph.seg_T), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int nfin = swi ? Th : ph.seg_T;
+    const uint32_t need = swi ? 2u * (uint32_t)ph.S : (uint32_t)S_eff;
+    if (swi) {  // pairs in batches: wait for all of a batch's counts, then one round of loads for all
+      constexpr int kSwiBatch = NK == 2 ? 5 : 2;
+      for (int t0 = blockIdx.x; t0 < nfin; t0 += kSwiBatch * gridDim.x) {
+        int n = 0;
+        bool ok = true;
+        for (int t = t0; ok && n < kSwiBatch && t < nfin; t += gridDim.x, ++n) ok = fin_wait(a, cnt0 + t, need);
+        if (!ok) break;
+        swiglu_pairs<NK>(a, ph, t0, n);
+        if (lane < n) __hip_atomic_store(cnt0 + t0 + lane * gridDim.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      for (int t = blockIdx.x; t < nfin; t += gridDim.x) {
+        uint32_t *cnt = cnt0 + t;
+        if (!fin_wait(a, cnt, need)) break;
+        finalise_tiles<NK>(a, ph, t, S_eff, TN, best_v[0], best_i[0]);
+        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next step
+      }
     }
   }
   if (ph.out == OUT_LOGITS) {  // per-workgroup argmax candidate of each row (first index on ties)
@@ -1125,6 +1234,7 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
   float *al = kh + kMaxRows * 128;              // [nj][dk] decay per key channel
   float *be = al + kMaxRows * 128;              // [nj] write strength
   float *vv = be + kMaxRows;                    // [nj][RPU] values of the block's rows
+  float *ov = vv + kMaxRows * 64;               // [nj][RPU] outputs, staged by the sync wave
   const int c0 = lane * 2;
   for (int u = u0; u < u1; ++u) {
     const int b = u / (Hl * RB), h = (u / RB) % Hl, rb = u % RB;
@@ -1190,7 +1300,10 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
           st.y += delta * k2.y;
           const float o = wave_sum(st.x * q2.x + st.y * q2.y);
           const int orow = a.verify ? j : b;
-          if (lane == 0) st_c(a.mix + (size_t)orow * a.mix_stride + h * dv + r, o);
+          if (lane == 0) {
+            st_c(a.mix + (size_t)orow * a.mix_stride + h * dv + r, o);
+            ov[j * RPU + rl] = o;
+          }
           if (a.verify) {
             float *sn = a.snap + ((((size_t)ph.lin_idx * kMaxRows + j) * Hl + h) * dv + r) * dk + c0;
             st_c(sn, st.x);
@@ -1201,6 +1314,11 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
       }
     }
     lds_barrier();  // LDS gates are reused by the next unit
+    if (SYNCW && ph.stg_out)  // the block's outputs, staged for the output projection (read before the
+      for (int i = lane; i < nj * RPU; i += 64) {  // next unit's first barrier, after which they are rewritten)
+        const int j = i / RPU, rr = rb * RPU + (i - j * RPU);
+        stg_put(a.stg[1], R, h * dv + rr, a.verify ? j : b, ov[i]);
+      }
   }
 }
 
@@ -1655,6 +1773,7 @@ __device__ __forceinline__ void mla_phase(CArgs &a, const Phase &ph, char *smem)
 
 // Log-sum-exp merge of split-KV partials (m, l, sum p v) over chunks, per (row, query head): grouped
 // query attention (head width hd) or latent attention (latent rank).
+template <bool SYNCW>  // SYNCW: the sync wave's copy (it also writes the staged outputs)
 __device__ __forceinline__ void merge_phase(CArgs &a, const Phase &ph, char *smem) {
   const bool mla = ph.type == PH_MLA_MERGE;
   const int R = a.R, nq = mla ? ph.heads : a.nq, hd = mla ? ph.rank : a.hd, NC = ph.n_chunks, W = hd + 2;
@@ -1663,6 +1782,7 @@ __device__ __forceinline__ void merge_phase(CArgs &a, const Phase &ph, char *sme
   const int u0 = (int)(((int64_t)U * wg) / G), u1 = (int)(((int64_t)U * (wg + 1)) / G);
   float *pl = reinterpret_cast<float *>(smem);  // [NC][hd + 2]
   float *wt = pl + NC * W;                       // [NC] weights, then [1] total
+  float *ov = wt + NC + 1;                       // [hd] outputs, staged by the sync wave
   for (int u = u0; u < u1; ++u) {
     const int row = u / nq, h = u % nq;
     const float *p = a.attn + ((size_t)row * nq + h) * NC * W;
@@ -1704,10 +1824,17 @@ __device__ __forceinline__ void merge_phase(CArgs &a, const Phase &ph, char *sme
       float o = 0.0f;
       for (int c = 0; c < NC; ++c) o += pl[c * W + 2 + i] * wt[c];
       st_c(a.mix + (size_t)row * a.mix_stride + h * hd + i, o / L);
+      if (ph.stg_out) ov[i] = o / L;
+    }
+    if (ph.stg_out) {
+      lds_barrier();
+      if (SYNCW)
+        for (int i = tid & 63; i < hd; i += 64) stg_put(a.stg[1], R, h * hd + i, row, ov[i]);
     }
   }
 }
 
+template <bool SYNCW>  // the sync wave embeds (16 values per unit); the other waves only keep the barriers
 __device__ __forceinline__ void embed_phase(CArgs &a, const Phase &ph, char *smem) {
   const int R = a.R, H = a.H, nt = H / kTileRows;
   const int U = R * nt;
@@ -1718,25 +1845,27 @@ __device__ __forceinline__ void embed_phase(CArgs &a, const Phase &ph, char *sme
   for (int u = u0; u < u1; ++u) {
     const int row = u / nt, t = u % nt;
     lds_barrier();
-    if (tid < kTileRows) {
-      const int n = t * kTileRows + tid;
+    const int ln = tid & 63;
+    if (SYNCW && ln < kTileRows) {
+      const int n = t * kTileRows + ln;
       float v;
       if (a.V > 0) {
         // the first step embeds the caller's tokens; a later step of a multi-step launch the token the
         // previous step emitted (written by workgroup 0 before the grid barrier)
         int tok = ph.step == 0 ? a.tokens[row] : ld_ci(a.loop_tokens + (size_t)(ph.step - 1) * a.R + row);
         if (tok < 0 || tok >= a.V) {  // out-of-range token: report, read row 0 instead of faulting
-          if (tid == 0) { st_ci(a.status + 1, -2); st_ci(a.status + 0, 1 /* MK_E_ARG */); }
+          if (ln == 0) { st_ci(a.status + 1, -2); st_ci(a.status + 0, 1 /* MK_E_ARG */); }
           tok = 0;
         }
         v = bf2f(E[(size_t)tok * H + n]);
       }
       else v = a.hidden_in[(size_t)row * H + n];
       st_c(a.x + (size_t)row * H + n, v);
-      sq[tid] = v * v;
+      if (ph.stg_out) stg_put_x(a, ph, n, row, v);
+      sq[ln] = v * v;
     }
     lds_barrier();
-    if (tid == 0) {
+    if (SYNCW && ln == 0) {
       float s = 0.0f;
       for (int i = 0; i < kTileRows; ++i) s += sq[i];
       st_c(a.ss + (size_t)row * nt + t, s);
@@ -1808,14 +1937,14 @@ using namespace mk;
 template <bool SYNCW>  // SYNCW: the sync wave's copy of the phase loop
 __device__ __forceinline__ void common_phase(CArgs &a, const Phase &ph, char *smem) {
   switch (ph.type) {
-    case PH_EMBED: embed_phase(a, ph, smem); break;
+    case PH_EMBED: embed_phase<SYNCW>(a, ph, smem); break;
     case PH_DELTA: delta_phase<SYNCW>(a, ph, smem); break;
     case PH_ATTN:
       if (a.hd == 64) attn_phase<64, SYNCW>(a, ph, smem);
       else attn_phase<128, SYNCW>(a, ph, smem);
       break;
     case PH_MERGE:
-    case PH_MLA_MERGE: merge_phase(a, ph, smem); break;
+    case PH_MLA_MERGE: merge_phase<SYNCW>(a, ph, smem); break;
     case PH_MLA: mla_phase(a, ph, smem); break;
     case PH_FINAL: final_phase(a, ph, smem); break;
     case PH_HIDDEN_OUT: hidden_out_phase(a); break;

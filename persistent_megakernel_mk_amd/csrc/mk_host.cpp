@@ -143,14 +143,15 @@ struct mk_ctx {
   Slot embed, final_norm, lm_head;
   uint32_t global_need = 0, global_have = 0;
   int64_t packed_bytes = 0;
-  int n_lin = 0, n_resid = 0, n_moe = 0, max_rows = 1;
+  int n_lin = 0, n_resid = 0, n_moe = 0, n_swi = 0, max_rows = 1;  // n_swi: dense FFN layers (SwiGLU finalisers)
   std::vector<int> lin_index;  // per layer: index among linear-attention layers (-1 otherwise)
   int mix_stride = 0;
   Schedule sched[kMaxBatch + 1];  // by row count
   // scratch layout (byte offsets)
   int64_t o_rope_mla = 0, o_loop = 0;
   int64_t o_status = 0, o_bar = 0, o_fin = 0, o_x = 0, o_ss = 0, o_part[3] = {0, 0, 0}, o_mix = 0, o_attn = 0,
-          o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxBatch + 1] = {}, scratch_bytes = 0;
+          o_cand = 0, o_rope = 0, o_snap = 0, o_ptrs = 0, o_phases[kMaxBatch + 1] = {}, scratch_bytes = 0,
+          o_stg[3] = {0, 0, 0};
   int64_t kv_bytes = 0, lin_bytes = 0, latent_bytes = 0;
   // bound buffers
   bool bound = false;
@@ -317,7 +318,8 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       const int nc = (f.max_ctx + cs - 1) / cs;
       const int64_t units = (int64_t)nseq_max * f.n_kv_heads * nc;
       const double cost = (double)((units + G - 1) / G) * (cs + 64) + 1e-3 * nc;
-      if ((int64_t)nc * (f.head_dim + 2) * 4 + (nc + 1) * 4 > kLdsBytes) continue;  // merge stages all chunks in LDS
+      if ((int64_t)nc * (f.head_dim + 2) * 4 + (nc + 1) * 4 + f.head_dim * 4 > kLdsBytes) continue;  // merge stages
+                                                                                                     // all chunks in LDS
       if (cost < best) { best = cost; sc.chunk = cs; sc.n_chunks = nc; }
     }
     if (sc.chunk == 0) return fail(MK_E_CAPACITY, "no split-KV chunking fits max_ctx %d", f.max_ctx);
@@ -532,6 +534,44 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
     ho.type = PH_HIDDEN_OUT;
     sc.phases.push_back(ho);
   }
+  // staged activations: each product whose activation is the RMSNorm of x, a mixer output (one for
+  // all its rows) or a dense SwiGLU copies it from a buffer its producer wrote in the LDS layout
+  {
+    const int pairs = f.ffn / kTileRows;
+    int x_writer = -1, mix_writer = -1, n_swi = 0;
+    for (size_t i = 0; i < sc.phases.size(); ++i) {
+      Phase &p = sc.phases[i];
+      if (p.type == PH_EMBED) {
+        x_writer = (int)i;
+      } else if (p.type == PH_DELTA || p.type == PH_MERGE) {
+        mix_writer = (int)i;
+      } else if (p.type == PH_GEMV) {
+        const bool shared = p.seg == SEG_NONE || p.act == ACT_NORM;
+        if (p.act == ACT_NORM && shared && x_writer >= 0) {
+          Phase &w = sc.phases[(size_t)x_writer];
+          if (!w.stg_out) {
+            w.stg_out = 1;
+            w.stg_gain_off = p.gain_off;
+          }
+          if (w.stg_gain_off == p.gain_off) p.stg_in = STG_X;
+        } else if (p.act == ACT_MIX && p.seg == SEG_NONE && p.src_off == 0 && mix_writer >= 0) {
+          sc.phases[(size_t)mix_writer].stg_out = 1;
+          p.stg_in = STG_MIX;
+        } else if (p.act == ACT_SWIGLU && p.seg == SEG_NONE && i > 0) {
+          Phase &gu = sc.phases[i - 1];  // the dense gate|up product right before its down product
+          if (gu.type == PH_GEMV && gu.seg == SEG_NONE && gu.out == OUT_PART && gu.N == 2 * f.ffn && p.K == f.ffn &&
+              p.src_off == 0 && p.src_S == gu.S) {
+            gu.stg_out = 1;
+            gu.swi_cnt_off = (int32_t)((int64_t)resid * (f.hidden / kTileRows) + f.vocab / kTileRows + (int64_t)n_swi * pairs);
+            ++n_swi;
+            p.stg_in = STG_H;
+          }
+        }
+        if (p.out == OUT_RESID) x_writer = (int)i;
+      }
+    }
+    c->n_swi = n_swi;
+  }
   // the weight stream of the compute waves follows the product phases in order
   int next = -1;
   for (int i = (int)sc.phases.size() - 1; i >= 0; --i) {
@@ -632,6 +672,23 @@ mk_status layout(mk_ctx *c) {
   return MK_OK;
 }
 
+// Finaliser counters: 16-row tiles of each residual product, of the vocabulary, then the 16-row pairs
+// of each dense gate|up product whose SwiGLU is staged.
+int64_t fin_counters(const mk_ctx *c) {
+  const mk_config &f = c->cfg;
+  return (int64_t)c->n_resid * (f.hidden / kTileRows) + f.vocab / kTileRows + (int64_t)c->n_swi * (f.ffn / kTileRows);
+}
+
+// Staged activation buffers at R rows: [K / 8][C][8] bf16 each (C columns of the B operand).
+int act_columns(int R) { return R <= kMaxRows ? 2 * R : 32; }
+void stg_sizes(const mk_ctx *c, int R, int64_t (&bytes)[3]) {
+  const mk_config &f = c->cfg;
+  const int64_t C = act_columns(R);
+  bytes[0] = (int64_t)f.hidden * C * 2;
+  bytes[1] = (int64_t)c->mix_stride * C * 2;
+  bytes[2] = c->n_swi > 0 ? (int64_t)f.ffn * C * 2 : 0;
+}
+
 mk_status scratch_layout(mk_ctx *c) {
   const mk_config &f = c->cfg;
   const int R = c->max_rows, H = f.hidden, G = c->G;
@@ -651,8 +708,13 @@ mk_status scratch_layout(mk_ctx *c) {
   }
   c->o_status = take(256);
   c->o_bar = take(9 * 128);
-  c->o_fin = take(((int64_t)c->n_resid * (H / kTileRows) + f.vocab / kTileRows) * 4);
+  c->o_fin = take(fin_counters(c) * 4);
   c->o_x = take((int64_t)R * H * 4);
+  {
+    int64_t sb[3];
+    stg_sizes(c, R, sb);
+    for (int i = 0; i < 3; ++i) c->o_stg[i] = take(sb[i]);
+  }
   c->o_ss = take((int64_t)R * (H / kTileRows) * 4);
   for (int i = 0; i < 3; ++i) c->o_part[i] = take(part[i] * 4);
   c->o_mix = take((int64_t)R * c->mix_stride * 4);
@@ -816,6 +878,7 @@ void fill_args(mk_ctx *c, StepArgs &a, int R, int verify, const mk_step_io *io) 
   a.cand = reinterpret_cast<float *>(c->scratch + c->o_cand);
   a.rope = reinterpret_cast<const float *>(c->scratch + c->o_rope);
   a.snap = reinterpret_cast<float *>(c->scratch + c->o_snap);
+  for (int i = 0; i < 3; ++i) a.stg[i] = reinterpret_cast<uint16_t *>(c->scratch + c->o_stg[i]);
   void **ptrs = reinterpret_cast<void **>(c->scratch + c->o_ptrs);
   a.kc = ptrs;
   a.vc = ptrs + MK_MAX_LAYERS;
@@ -878,7 +941,7 @@ mk_status check_step(mk_ctx *c, const mk_step_io *io, int R, int nseq, int nrow)
 mk_status reset_counters(mk_ctx *c, hipStream_t st) {
   HIP_TRY(hipMemsetAsync(c->scratch + c->o_status, 0, 256, st));
   HIP_TRY(hipMemsetAsync(c->scratch + c->o_bar, 0, 9 * 128, st));
-  HIP_TRY(hipMemsetAsync(c->scratch + c->o_fin, 0, ((size_t)c->n_resid * (c->cfg.hidden / kTileRows) + c->cfg.vocab / kTileRows) * 4, st));
+  HIP_TRY(hipMemsetAsync(c->scratch + c->o_fin, 0, (size_t)fin_counters(c) * 4, st));
   c->bar_done = 0;
   c->needs_reset = false;
   return MK_OK;
@@ -940,7 +1003,7 @@ mk_status noalloc_init(int device) {
 // Byte offsets of one step's working set at R rows inside the library-held array (the same regions,
 // sized for R rather than for the context's largest row count, as the bound workspace holds).
 struct NoAllocLayout {
-  int64_t bar, fin, x, ss, part[3], mix, attn, cand, total;
+  int64_t bar, fin, x, ss, part[3], mix, attn, cand, stg[3], total;
 };
 
 NoAllocLayout noalloc_layout(const mk_ctx *c, int R) {
@@ -958,13 +1021,18 @@ NoAllocLayout noalloc_layout(const mk_ctx *c, int R) {
   if (s.mla_chunks > 0) attn = std::max<int64_t>(attn, (int64_t)R * f.mla_heads * s.mla_chunks * (f.kv_rank + 2));
   NoAllocLayout L;
   L.bar = take(9 * 128);
-  L.fin = take(((int64_t)c->n_resid * (H / kTileRows) + f.vocab / kTileRows) * 4);
+  L.fin = take(fin_counters(c) * 4);
   L.x = take((int64_t)R * H * 4);
   L.ss = take((int64_t)R * (H / kTileRows) * 4);
   for (int i = 0; i < 3; ++i) L.part[i] = take(s.part_floats[i] * 4);
   L.mix = take((int64_t)R * c->mix_stride * 4);
   L.attn = take(attn * 4);
   L.cand = take((int64_t)c->G * R * 2 * 4);
+  {
+    int64_t sb[3];
+    stg_sizes(c, R, sb);
+    for (int i = 0; i < 3; ++i) L.stg[i] = take(sb[i]);
+  }
   L.total = off;
   return L;
 }
@@ -1287,6 +1355,7 @@ mk_status mk_decode_step_noalloc(mk_ctx *c, const mk_step_io *io, int batch, voi
   a.mix = reinterpret_cast<float *>(base + L.mix);
   a.attn = reinterpret_cast<float *>(base + L.attn);
   a.cand = reinterpret_cast<float *>(base + L.cand);
+  for (int i = 0; i < 3; ++i) a.stg[i] = reinterpret_cast<uint16_t *>(base + L.stg[i]);
   return launch_step(c, a, st);
 }
 

@@ -111,7 +111,18 @@ struct Phase {
   int32_t mla_src;                      // partial buffer of the absorbed queries
   int32_t step;       // decode step of a multi-step launch this phase belongs to (0 in a one-step table)
   int32_t chunk_verify;  // delta rule: state rows per unit in a verify block (chunk: in a decode step)
+  // ---- staged activations ----
+  // A product's activation fragments (the B operand: bf16 high and low halves of each row's value, in
+  // the LDS layout) can be written to a global buffer by the phase that produces its input, so that
+  // staging them is one copy of the product's K slice into LDS instead of a gather, sum and conversion
+  // in every workgroup.
+  int32_t stg_in;        // StgBuf the product copies its activation from (STG_NONE: formed as before)
+  int64_t stg_gain_off;  // x writers: byte offset of the bf16 gain of the RMSNorm that reads x next
+  int32_t stg_out;       // producer of a staged buffer: x writers (embed, residual products) write x times
+                         // that gain, delta / merge phases their output, a dense gate|up product its SwiGLU
+  int32_t swi_cnt_off;   // dense gate|up product with stg_out: finaliser counters of its 16-row pairs
 };
+enum StgBuf : int32_t { STG_NONE = 0, STG_X = 1, STG_MIX = 2, STG_H = 3 };
 
 struct StepArgs {
   const Phase *phases;
@@ -137,6 +148,9 @@ struct StepArgs {
   float *cand;         // argmax candidates [G][R][2]
   const float *rope;   // [max_ctx][hd/2][2] cos, sin
   float *snap;         // verify snapshots [lin layers][8][heads][d_v][d_k]
+  uint16_t *stg[3];    // staged activations (x times the next gain, mixer output, SwiGLU output), each
+                       // [K / 8][C][8] bf16 with C = 2R columns up to 8 rows (high halves, then low),
+                       // 32 above (two groups of 8 rows, 16 columns each)
   void *const *kc;     // per layer K cache pointers
   void *const *vc;
   void *const *ls;     // per layer linear states
