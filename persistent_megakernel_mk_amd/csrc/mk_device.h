@@ -248,8 +248,10 @@ __device__ __forceinline__ void unit_range(int U, int S, int &s, int &u0, int &u
   const int per = (int)gridDim.x / S, wg = blockIdx.x;
   s = wg / per;
   const int wl = wg - s * per;
-  u0 = (int)(((int64_t)U * wl) / per);
-  u1 = (int)(((int64_t)U * (wl + 1)) / per);
+  // shares (1024 + kXcdSkew) for even, (1024 - kXcdSkew) for odd workgroups: prefix 1024 i + skew (i & 1)
+  const int64_t tot = 1024 * (int64_t)per + kXcdSkew * (per & 1);
+  u0 = (int)(((int64_t)U * (1024 * (int64_t)wl + kXcdSkew * (wl & 1))) / tot);
+  u1 = (int)(((int64_t)U * (1024 * (int64_t)(wl + 1) + kXcdSkew * ((wl + 1) & 1))) / tot);
 }
 
 // Residual products finalise each tile in its last contributor. The workgroups of different k-splits
@@ -481,11 +483,12 @@ __device__ __forceinline__ void stream_take(Stream &st, CArgs &a, const char *sm
         CPhase *ph = cphase(a, st.q);
         const int per = (int)gridDim.x / ph->S;
         const int s = (int)blockIdx.x / per;
-        if (st.seg < 0) {
-          const int wl = (int)blockIdx.x - s * per;
+        if (st.seg < 0) {  // back to the range's first tile
+          int s1, w0, w1;
+          unit_range(ph->T, ph->S, s1, w0, w1);
           st.seg = 0;
           st.seg_left = 0x40000000;
-          stream_at(st, a, ph, smem, s, 0, (int)(((int64_t)ph->T * wl) / per), wave);
+          stream_at(st, a, ph, smem, s, 0, w0, wave);
         } else {
           ++st.seg;
           st.seg_left = ph->seg_T;
