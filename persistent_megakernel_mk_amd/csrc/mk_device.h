@@ -1055,12 +1055,32 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   if (nunits > 0) prep_act<WIDE>(a, ph, s, u0, u1, smem);
   lds_barrier();  // activation fragments ready, handoff counters cleared
   if (ph.act == ACT_NORM) {  // 1/rms of each row from the per-tile sums of squares (while the waves stream)
+    // every row's tile sums are loaded together, two tiles per lane at a time (one memory round per 128
+    // tiles, not one per row), and added in tile order as before
     const int nt = a.H / kTileRows;
-    for (int b = 0; b < R; ++b) {
-      float v = 0.0f;
-      for (int t = lane; t < nt; t += 64) v += ld_c(a.ss + (size_t)b * nt + t);
-      v = wave_sum(v);
-      if (lane == 0) rstd[b] = 1.0f / sqrtf(v / (float)a.H + a.eps);
+    float v[kMaxBatch];
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) v[b] = 0.0f;
+    for (int t0 = lane; t0 < nt; t0 += 128) {
+      float x[2][kMaxBatch];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int b = 0; b < kMaxBatch; ++b) {
+          const int t = t0 + 64 * q;
+          x[q][b] = (b < R && t < nt) ? ld_c(a.ss + (size_t)b * nt + t) : 0.0f;
+        }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int b = 0; b < kMaxBatch; ++b)
+          if (t0 + 64 * q < nt) v[b] += x[q][b];
+    }
+#pragma unroll
+    for (int b = 0; b < kMaxBatch; ++b) {
+      if (b >= R) continue;
+      const float w = wave_sum(v[b]);
+      if (lane == 0) rstd[b] = 1.0f / sqrtf(w / (float)a.H + a.eps);
     }
     wave_lds_sync();
   }
