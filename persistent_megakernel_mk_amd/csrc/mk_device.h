@@ -71,6 +71,36 @@ __device__ __forceinline__ void add8(float (&acc)[8], const float *p) {
   acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
   acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
 }
+
+// Sums over the k-split partials of an earlier product (S of them, stride floats apart), in k-split
+// order as a loop would, but with the loads of CH splits in flight together: a runtime-length loop of
+// dependent adds waits for each load in turn. (CH is kept small where the weight ring is live.)
+template <int CH>
+__device__ __forceinline__ float sum_splits(const float *p, size_t stride, int S) {
+  float v = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float x[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) x[i] = s0 + i < S ? ld_c(p + (size_t)(s0 + i) * stride) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (s0 + i < S) v += x[i];
+  }
+  return v;
+}
+template <int CH>
+__device__ __forceinline__ float2 sum_splits2(const float *p, size_t stride, int S) {
+  float2 v = make_float2(0.0f, 0.0f);
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float2 x[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) x[i] = s0 + i < S ? ld_c2(p + (size_t)(s0 + i) * stride) : make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+      if (s0 + i < S) { v.x += x[i].x; v.y += x[i].y; }
+  }
+  return v;
+}
 __device__ __forceinline__ uint32_t ld_cu(const uint32_t *p) {
   return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -121,6 +151,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0)), r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
   const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32)), r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
   return (r0 + r1) + (r2 + r3);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+// The (value, index) pair with the larger value (the smaller index on equal values) over the wave, in
+// every lane: the same DPP row exchanges as wave_sum, then the four row results. The choice is symmetric,
+// so the order of the exchanges does not change the result.
+__device__ __forceinline__ void wave_argmax(float &v, int &e) {
+  auto take = [&](float ov, int oe) {
+    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
+  };
+  take(dpp_f<0xB1>(v), dpp_i<0xB1>(e));
+  take(dpp_f<0x4E>(v), dpp_i<0x4E>(e));
+  take(dpp_f<0x141>(v), dpp_i<0x141>(e));
+  take(dpp_f<0x140>(v), dpp_i<0x140>(e));
+  const int vb = __float_as_int(v);
+  const float v1 = __int_as_float(__builtin_amdgcn_readlane(vb, 16)), v2 = __int_as_float(__builtin_amdgcn_readlane(vb, 32));
+  const float v3 = __int_as_float(__builtin_amdgcn_readlane(vb, 48));
+  const int e1 = __builtin_amdgcn_readlane(e, 16), e2 = __builtin_amdgcn_readlane(e, 32), e3 = __builtin_amdgcn_readlane(e, 48);
+  v = __int_as_float(__builtin_amdgcn_readlane(vb, 0));
+  e = __builtin_amdgcn_readlane(e, 0);
+  take(v1, e1);
+  take(v2, e2);
+  take(v3, e3);
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -276,11 +332,7 @@ __device__ __forceinline__ void compute_route(CArgs &a, const Phase &ph, char *s
   const float *zp = part_of(a, ph.z_part);
   for (int b = wave; b < R; b += kWavesTotal) {
     float *zr = zl + b * E;
-    for (int e = lane; e < E; e += 64) {
-      float v = 0.0f;
-      for (int s2 = 0; s2 < ph.z_S; ++s2) v += ld_c(zp + ((size_t)s2 * R + b) * ph.z_N + e);
-      zr[e] = v;
-    }
+    for (int e = lane; e < E; e += 64) zr[e] = sum_splits<8>(zp + (size_t)b * ph.z_N + e, (size_t)R * ph.z_N, ph.z_S);
     wave_lds_sync();
     float total = 0.0f;
     for (int t = 0; t < K; ++t) {
@@ -290,14 +342,8 @@ __device__ __forceinline__ void compute_route(CArgs &a, const Phase &ph, char *s
         const float v = zr[e];
         if (v > bv || be == 0x7fffffff) { bv = v; be = e; }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oe = __shfl_xor(be, o);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
+      wave_argmax(bv, be);
       be = __builtin_amdgcn_readfirstlane(be);
-      bv = __shfl(bv, 0);
       const float sg = sigmoidf_(bv);
       total += sg;
       if (lane == 0) {
@@ -1273,30 +1319,25 @@ __device__ __forceinline__ void delta_phase(CArgs &a, const Phase &ph, char *sme
       const int row = a.verify ? j : b;
       if (kind < 2) {
         const int off = (kind == 0 ? ph.q_off : ph.k_off) + h * dk + c0;
-        float x0 = 0.0f, x1 = 0.0f;
-        for (int s2 = 0; s2 < ph.src_S; ++s2) {
-          const float2 p2 = ld_c2(src + ((size_t)s2 * R + row) * ph.src_N + off);
-          x0 += p2.x;
-          x1 += p2.y;
-        }
+        const float2 p2 = sum_splits2<4>(src + (size_t)row * ph.src_N + off, (size_t)R * ph.src_N, ph.src_S);
+        const float x0 = p2.x, x1 = p2.y;
         const float n = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) + 1e-6f);
         float *dst = (kind == 0 ? qh : kh) + j * 128 + c0;
         dst[0] = x0 * n;
         dst[1] = x1 * n;
       } else {
-        float a0 = 0.0f, a1 = 0.0f, bb = 0.0f, vr = 0.0f;
-        for (int s2 = 0; s2 < ph.src_S; ++s2) {
-          const float *pr = src + ((size_t)s2 * R + row) * ph.src_N;
-          if (ph.per_channel_gate) {
-            const float2 p2 = ld_c2(pr + ph.a_off + h * dk + c0);
-            a0 += p2.x;
-            a1 += p2.y;
-          } else {
-            a0 += ld_c(pr + ph.a_off + h);
-          }
-          bb += ld_c(pr + ph.b_off + h);
-          if (lane < RPU) vr += ld_c(pr + ph.v_off + h * dv + rb * RPU + lane);
+        float a0, a1 = 0.0f, vr = 0.0f;
+        const float *pr = src + (size_t)row * ph.src_N;
+        const size_t sst = (size_t)R * ph.src_N;
+        if (ph.per_channel_gate) {
+          const float2 p2 = sum_splits2<4>(pr + ph.a_off + h * dk + c0, sst, ph.src_S);
+          a0 = p2.x;
+          a1 = p2.y;
+        } else {
+          a0 = sum_splits<4>(pr + ph.a_off + h, sst, ph.src_S);
         }
+        const float bb = sum_splits<4>(pr + ph.b_off + h, sst, ph.src_S);
+        if (lane < RPU) vr = sum_splits<4>(pr + ph.v_off + h * dv + rb * RPU + lane, sst, ph.src_S);
         if (!ph.per_channel_gate) a1 = a0;
         al[j * 128 + c0] = __expf(-softplusf_(a0));
         al[j * 128 + c0 + 1] = ph.per_channel_gate ? __expf(-softplusf_(a1)) : al[j * 128 + c0];
