@@ -1074,6 +1074,74 @@ __device__ __forceinline__ void swiglu_pairs(CArgs &a, const Phase &ph, int t0, 
     }
 }
 
+// Logits of a product split over k (counted after the workgroup's units): the designated workgroup of
+// tiles t0, t0 + G, ... (n of them, up to kLogitBatch) sums each tile's partials in k-split order, with
+// two k-splits' loads for all n tiles in flight at a time, stores the logits and keeps each row's first
+// maximum (lane b holds row b's).
+template <int NK>
+__device__ __forceinline__ void logit_tiles(CArgs &a, const Phase &ph, int t0, int n, float &best_v, int &best_i) {
+  constexpr int kLogitBatch = NK == 2 ? 8 : 4;
+  const int R = a.R, lane = threadIdx.x & 63, G = gridDim.x;
+  const float *pp = part_of(a, ph.dst_part);
+  float acc[kLogitBatch][NK];
+#pragma unroll
+  for (int i = 0; i < kLogitBatch; ++i)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) acc[i][k] = 0.0f;
+  for (int s2 = 0; s2 < ph.S; s2 += 2) {
+    const bool two = s2 + 1 < ph.S;
+    float p[kLogitBatch][NK][2];
+#pragma unroll
+    for (int i = 0; i < kLogitBatch; ++i)
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int idx = lane + 64 * k, row = idx & 15, b = idx < 16 * R ? idx >> 4 : 0;  // (a valid dummy)
+          const int t = t0 + (i < n ? i : 0) * G;
+          p[i][k][h] = ld_c(pp + ((size_t)(two ? s2 + h : s2) * R + b) * ph.N + (size_t)t * kTileRows + row);
+        }
+#pragma unroll
+    for (int i = 0; i < kLogitBatch; ++i)
+#pragma unroll
+      for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 1 && !two) continue;
+          acc[i][k] += p[i][k][h];
+        }
+  }
+  float kb_v[NK];  // per lane: the best of its (row b) values over the n tiles, in increasing row order
+  int kb_i[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) { kb_v[k] = -INFINITY; kb_i[k] = 0x7fffffff; }
+#pragma unroll
+  for (int i = 0; i < kLogitBatch; ++i)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int idx = lane + 64 * k;
+      if (i < n && idx < 16 * R) {
+        const int nr = (t0 + i * G) * kTileRows + (idx & 15);
+        a.logits[(size_t)(idx >> 4) * a.V + nr] = acc[i][k];
+        if (acc[i][k] > kb_v[k]) { kb_v[k] = acc[i][k]; kb_i[k] = nr; }
+      }
+    }
+  for (int b = 0; b < R; ++b) {  // per row: the first maximum over the wave, kept by lane b
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+      if (lane + 64 * k < 16 * R && ((lane + 64 * k) >> 4) == b) { bv = kb_v[k]; bi = kb_i[k]; }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == b && (bv > best_v || (bv == best_v && bi < best_i))) { best_v = bv; best_i = bi; }
+  }
+}
+
 // sync wave: activation staging (with the compute waves), norm statistics, per-unit reduction and
 // stores, finalisation
 template <bool WIDE>
@@ -1144,10 +1212,12 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   const int nrot = u1 - u0, r0 = rotated(ph) ? rot_start(s, ph.S, nrot) : 0;
   const bool fin = needs_finalise(ph);
   const bool direct_resid = ph.out == OUT_RESID && S_eff == 1;
-  // expert down products: a tile has one partial per (expert, k-split) and a workgroup many small
-  // units, so contributions are counted once after all of this workgroup's units, and each tile is
-  // finalised by one designated workgroup (tile t by workgroup t mod G) once its count is complete
-  const bool deferred = fin && expert && !direct_resid;
+  // expert down products (a tile has one partial per (expert, k-split) and a workgroup many small units)
+  // and logits split over k (a workgroup has dozens of units, and a per-unit acknowledgement and counter
+  // round trip would outlast the unit's weights): contributions are counted once after all of this
+  // workgroup's units, and each tile is finalised by one designated workgroup (tile t by workgroup
+  // t mod G) once its count is complete
+  const bool deferred = fin && (expert || ph.out == OUT_LOGITS) && !direct_resid;
   const bool swi = ph.out == OUT_PART && ph.stg_out;  // dense gate|up: SwiGLU of complete pairs, staged
   for (int unit = 0; unit < nrot; ++unit) {
     const int u = u0 + (r0 + unit < nrot ? r0 + unit : r0 + unit - nrot);
@@ -1224,9 +1294,10 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
     }
   }
   if (deferred || swi) {
-    // expert down tiles: one count per (segment, k-split); dense gate|up pairs: one per (gate or up
-    // tile, k-split). All of this workgroup's partials are acknowledged once, then counted; each tile
-    // or pair is finalised by its designated workgroup (index mod G) when its count is complete.
+    // expert down tiles: one count per (segment, k-split); logit tiles: one per k-split; dense gate|up
+    // pairs: one per (gate or up tile, k-split). All of this workgroup's partials are acknowledged once,
+    // then counted; each tile or pair is finalised by its designated workgroup (index mod G) when its
+    // count is complete.
     __builtin_amdgcn_s_waitcnt(0);
     const int Th = ph.T / 2;
     uint32_t *cnt0 = a.fin + (swi ? ph.swi_cnt_off : ph.cnt_off);
@@ -1244,6 +1315,16 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
         for (int t = t0; ok && n < kSwiBatch && t < nfin; t += gridDim.x, ++n) ok = fin_wait(a, cnt0 + t, need);
         if (!ok) break;
         swiglu_pairs<NK>(a, ph, t0, n);
+        if (lane < n) __hip_atomic_store(cnt0 + t0 + lane * gridDim.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (ph.out == OUT_LOGITS) {  // tiles in batches, like the pairs
+      constexpr int kLogitBatch = NK == 2 ? 8 : 4;
+      for (int t0 = blockIdx.x; t0 < nfin; t0 += kLogitBatch * gridDim.x) {
+        int n = 0;
+        bool ok = true;
+        for (int t = t0; ok && n < kLogitBatch && t < nfin; t += gridDim.x, ++n) ok = fin_wait(a, cnt0 + t, need);
+        if (!ok) break;
+        logit_tiles<NK>(a, ph, t0, n, best_v[0], best_i[0]);
         if (lane < n) __hip_atomic_store(cnt0 + t0 + lane * gridDim.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     } else {
