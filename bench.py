@@ -575,7 +575,9 @@ def main() -> int:
         "config": {"workload": describe(cfg, batches[0]), "batch": batches[0], "kv_positions": cfg.ctx},
         "roofline": {"bound": "hbm", "achieved": round(h["alg_gbs"], 1), "peak": accounting.HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(h["alg_gbs"] / accounting.HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic() if (cfg.name == "c1" and batches[0] == 1) else None,
+                     # the counter profile covers the default workload only (c1, batch 1, its own cache length)
+                     "traffic": counter_traffic() if (cfg.name == "c1" and batches[0] == 1
+                                                      and cfg.ctx == synth.CONFIGS["c1"].ctx) else None,
                      "alg_bytes_per_launch": h["alg_bytes"], "kernel": "mk_step_kernel"},
         "cpu_baseline": cpu,
         "stream_read_ref": None if stream is None else {
