@@ -304,10 +304,8 @@ __device__ __forceinline__ void unit_range(int U, int S, int &s, int &u0, int &u
   const int per = (int)gridDim.x / S, wg = blockIdx.x;
   s = wg / per;
   const int wl = wg - s * per;
-  // shares (1024 + kXcdSkew) for even, (1024 - kXcdSkew) for odd workgroups: prefix 1024 i + skew (i & 1)
-  const int64_t tot = 1024 * (int64_t)per + kXcdSkew * (per & 1);
-  u0 = (int)(((int64_t)U * (1024 * (int64_t)wl + kXcdSkew * (wl & 1))) / tot);
-  u1 = (int)(((int64_t)U * (1024 * (int64_t)(wl + 1) + kXcdSkew * ((wl + 1) & 1))) / tot);
+  u0 = (int)(((int64_t)U * wl) / per);
+  u1 = (int)(((int64_t)U * (wl + 1)) / per);
 }
 
 // Residual products finalise each tile in its last contributor. The workgroups of different k-splits

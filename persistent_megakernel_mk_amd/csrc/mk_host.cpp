@@ -256,8 +256,7 @@ int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_
     const int nf = KF / S;
     const int64_t per_split = G / S;                     // workgroups per k-split
     const int64_t per = (U + per_split - 1) / per_split;  // units per workgroup (the cost estimate)
-    // the busiest workgroup's units (even workgroups take the larger shares)
-    const int64_t per_max = (U * (1024 + kXcdSkew) + 1024 * per_split - 1) / (1024 * per_split) + 1;
+    const int64_t per_max = per;  // the busiest workgroup's units
     if (per_max > kMaxUnits) continue;
     const int np = per_seg_act ? (int)std::min<int64_t>((per_max - 1 + segT - 1) / segT + 1, nseg) : 1;
     if (np > kMaxPieces) continue;
@@ -303,7 +302,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
   auto add_gemv = [&](Phase p, int buf) -> mk_status {
     if (p.S <= 0) return fail(MK_E_CAPACITY, "no k-split of a %dx%d product fits the on-chip budget at %d rows", p.N, p.K, R);
     const int64_t units = p.seg == SEG_EXPERT ? (int64_t)p.seg_T * (p.n_shared + std::min(p.n_exp, R * p.top_k)) : p.T;
-    if ((units * (1024 + kXcdSkew) + 1024 * (G / p.S) - 1) / (1024 * (G / p.S)) + 1 > kMaxUnits)
+    if ((units + G / p.S - 1) / (G / p.S) > kMaxUnits)
       return fail(MK_E_CAPACITY, "%dx%d product: too many units per workgroup", p.N, p.K);
     int64_t need = (int64_t)p.S * R * p.N;
     if (p.seg == SEG_EXPERT && p.out == OUT_RESID)  // one partial per (segment, k-split)

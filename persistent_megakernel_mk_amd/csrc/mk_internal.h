@@ -22,10 +22,6 @@ constexpr int kMaxRows = 8;               // rows of a verify block; rows whose 
                                           // as bf16 high and low halves (2 MFMA columns each)
 constexpr int kMaxBatch = 16;             // rows of a decode step; above kMaxRows each activation enters
                                           // products as one bf16 column (the 16 columns hold 16 rows)
-// Product units are split among a k-split's workgroups in contiguous ranges weighted by workgroup parity:
-// on MI355X workgroup i runs on XCD i mod 8, and the odd XCDs were measured to stream 4-6% slower than
-// the even ones, so even workgroups take (1024 + kXcdSkew) / 1024 shares and odd ones (1024 - kXcdSkew).
-constexpr int kXcdSkew = 24;
 constexpr int kMaxUnits = 512;            // product units (tile x k-split) per workgroup and phase
 constexpr int kMaxTopK = 16;              // routed experts per token
 constexpr int kMaxExperts = 1024;         // routed experts per MoE layer
