@@ -203,22 +203,22 @@ __device__ __forceinline__ void stg_put_x(CArgs &a, const Phase &ph, int n, int 
 }
 
 // ---------------------------------------------------------------------------------------------
-// grid barrier: two-level counters (8 groups, then one top counter), monotone across steps.
+// grid barrier: two-level counters (kBarGroups groups, then one top counter), monotone across steps.
 // Run by lane 0 of the sync wave; the caller brackets it with workgroup barriers.
 // ---------------------------------------------------------------------------------------------
 __device__ bool grid_arrive_wait(CArgs &a, uint32_t k, int phase) {
   const uint32_t G = gridDim.x;
-  const uint32_t groups = G < 8u ? G : 8u;
+  const uint32_t groups = G < (uint32_t)kBarGroups ? G : (uint32_t)kBarGroups;
   const uint32_t g = blockIdx.x % groups;
   const uint32_t cnt = G / groups + (g < (G % groups) ? 1u : 0u);
   uint32_t old = __hip_atomic_fetch_add(a.bar + g * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (old + 1u == k * cnt) __hip_atomic_fetch_add(a.bar + 8 * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old + 1u == k * cnt) __hip_atomic_fetch_add(a.bar + kBarGroups * 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t tgt = k * groups;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   bool ok = true;
   for (uint32_t it = 0;; ++it) {
     // the barrier word and (every 16th poll) the abort flag are loaded together
-    const uint32_t v = ld_cu(a.bar + 8 * 32);
+    const uint32_t v = ld_cu(a.bar + kBarGroups * 32);
     const int32_t ab = (it & 15u) == 15u ? ld_ci(a.status + 2) : 0;
     if ((int32_t)(v - tgt) >= 0) break;
     if (ab != 0) { ok = false; break; }

@@ -263,9 +263,9 @@ int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_
     const int C = R <= kMaxRows ? 2 * R : 32;  // B-operand columns: bf16 high and low halves, 16 per group of 8 rows
     if ((int64_t)np * nf * 64 * C > (R <= kMaxRows ? kActLdsBudgetNarrow : kActLdsBudget)) continue;
     // a residual product split over k also pays, per unit, the acknowledgement of its partials and the
-    // tile counter round trip (about ten fragment times); with one split the unit adds into the
+    // tile counter round trip (about five fragment times); with one split the unit adds into the
     // residual directly
-    const double fin = (resid && S > 1) ? 10.0 * per : 0.0;
+    const double fin = (resid && S > 1) ? 5.0 * per : 0.0;
     const double cost = (double)per * ((nf + kCWaves - 1) / kCWaves + 1.0) + fin + 0.01 * S;
     if (cost < best_cost) { best_cost = cost; best = S; best_pieces = np; }
   }
@@ -709,7 +709,7 @@ mk_status scratch_layout(mk_ctx *c) {
     if (s.mla_chunks > 0) attn = std::max<int64_t>(attn, (int64_t)r * f.mla_heads * s.mla_chunks * (f.kv_rank + 2));
   }
   c->o_status = take(256);
-  c->o_bar = take(9 * 128);
+  c->o_bar = take(kBarBytes);
   c->o_fin = take(fin_counters(c) * 4);
   c->o_x = take((int64_t)R * H * 4);
   {
@@ -942,7 +942,7 @@ mk_status check_step(mk_ctx *c, const mk_step_io *io, int R, int nseq, int nrow)
 
 mk_status reset_counters(mk_ctx *c, hipStream_t st) {
   HIP_TRY(hipMemsetAsync(c->scratch + c->o_status, 0, 256, st));
-  HIP_TRY(hipMemsetAsync(c->scratch + c->o_bar, 0, 9 * 128, st));
+  HIP_TRY(hipMemsetAsync(c->scratch + c->o_bar, 0, kBarBytes, st));
   HIP_TRY(hipMemsetAsync(c->scratch + c->o_fin, 0, (size_t)fin_counters(c) * 4, st));
   c->bar_done = 0;
   c->needs_reset = false;
@@ -1022,7 +1022,7 @@ NoAllocLayout noalloc_layout(const mk_ctx *c, int R) {
   if (f.n_q_heads > 0) attn = std::max<int64_t>(attn, (int64_t)R * f.n_q_heads * s.n_chunks * (f.head_dim + 2));
   if (s.mla_chunks > 0) attn = std::max<int64_t>(attn, (int64_t)R * f.mla_heads * s.mla_chunks * (f.kv_rank + 2));
   NoAllocLayout L;
-  L.bar = take(9 * 128);
+  L.bar = take(kBarBytes);
   L.fin = take(fin_counters(c) * 4);
   L.x = take((int64_t)R * H * 4);
   L.ss = take((int64_t)R * (H / kTileRows) * 4);

@@ -28,6 +28,11 @@ constexpr int kMaxExperts = 1024;         // routed experts per MoE layer
 constexpr int kMaxShared = 4;             // shared experts per MoE layer
 constexpr int kMaxSeg = kMaxShared + kMaxRows * kMaxTopK;  // expert segments of one MoE product phase
 constexpr int kMaxPieces = 4;             // activation pieces (segment x k-split) staged per workgroup
+// grid barrier: workgroups arrive at kBarGroups group counters (workgroup i at i mod kBarGroups), the
+// last arrival of a group at one top counter that every workgroup polls; counters 128 B apart. Four
+// groups of 64 measured faster than 2, 8 or 16 (16 slowest).
+constexpr int kBarGroups = 4;
+constexpr int kBarBytes = (kBarGroups + 1) * 128;
 
 enum PhaseType : int32_t {
   PH_EMBED = 1,      // residual x <- embedding rows (or hidden_in); per-tile sums of squares
@@ -135,7 +140,7 @@ struct StepArgs {
   int32_t barrier_base;            // barriers completed before phase_begin within this step
   const uint8_t *wbuf;
   // scratch regions
-  uint32_t *bar;       // 9 counters, 128 B apart (8 groups + top)
+  uint32_t *bar;       // kBarGroups group counters and the top counter, 128 B apart
   uint32_t *fin;       // finalizer counters
   int32_t *status;     // [0] status, [1] phase, [2] abort flag
   float *x;            // residual [R][H]
