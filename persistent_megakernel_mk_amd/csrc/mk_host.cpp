@@ -244,7 +244,7 @@ mk_status validate(const mk_config *c) {
 // time per unit for the cross-wave reduction). A product of nseg segments of segT tiles each gives every
 // segment its own activation when per_seg_act (one piece per segment a workgroup's units touch).
 int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_seg_act = false, int fpi = 1,
-                  int *pieces_out = nullptr, bool resid = false) {
+                  int *pieces_out = nullptr, bool resid = false, int consumer_rows = 0) {
   int best = -1, best_pieces = 1;
   double best_cost = 1e300;
   const int64_t U = (int64_t)segT * nseg;
@@ -266,14 +266,16 @@ int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_
     // tile counter round trip (about five fragment times); with one split the unit adds into the
     // residual directly
     const double fin = (resid && S > 1) ? 5.0 * per : 0.0;
-    const double cost = (double)per * ((nf + kCWaves - 1) / kCWaves + 1.0) + fin + 0.01 * S;
+    // a consumer that sums the k-split partials of every value it reads (the mixers read their inputs
+    // that way) pays for each split, per row
+    const double cost = (double)per * ((nf + kCWaves - 1) / kCWaves + 1.0) + fin + (double)S * consumer_rows + 0.01 * S;
     if (cost < best_cost) { best_cost = cost; best = S; best_pieces = np; }
   }
   if (pieces_out) *pieces_out = best_pieces;
   return best;
 }
 
-Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S) {
+Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S, int consumer_rows = 0) {
   const bool resid = out == OUT_RESID;
   Phase p;
   memset(&p, 0, sizeof(p));
@@ -283,7 +285,7 @@ Phase gemv_phase(const Slot &w, int act, int out, int R, int G, int max_S) {
   p.K = w.K;
   p.T = w.N / kTileRows;
   p.KF = w.K / kFragK;
-  p.S = choose_splits(p.T, 1, p.KF, R, G, max_S, false, 1, nullptr, resid);
+  p.S = choose_splits(p.T, 1, p.KF, R, G, max_S, false, 1, nullptr, resid, consumer_rows);
   p.nf = p.S > 0 ? p.KF / p.S : 0;
   p.act = act;
   p.out = out;
@@ -352,7 +354,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
   for (int l = 0; l < f.n_layers; ++l) {
     const LayerSlots &s = c->L[l];
     const int m = f.mixer[l];
-    Phase p = gemv_phase(s.mix_in, ACT_NORM, OUT_PART, R, G, 64);
+    Phase p = gemv_phase(s.mix_in, ACT_NORM, OUT_PART, R, G, 64, R);
     p.layer = l;
     p.gain_off = s.attn_norm.off;
     if (mk_status st = add_gemv(p, 0)) return st;
