@@ -267,7 +267,7 @@ int choose_splits(int segT, int nseg, int KF, int R, int G, int max_S, bool per_
     // residual directly
     const double fin = (resid && S > 1) ? 5.0 * per : 0.0;
     // a consumer that sums the k-split partials of every value it reads (the mixers read their inputs
-    // that way) pays for each split, per row
+    // that way, every workgroup's routing its router logits) pays for each split, per row
     const double cost = (double)per * ((nf + kCWaves - 1) / kCWaves + 1.0) + fin + (double)S * consumer_rows + 0.01 * S;
     if (cost < best_cost) { best_cost = cost; best = S; best_pieces = np; }
   }
@@ -465,7 +465,7 @@ mk_status build_schedule(mk_ctx *c, int R, Schedule &sc) {
       const int fmt_gu = gate_up_fmt(f), fmt_d = down_fmt(f);
       const int F = f.expert_ffn, H = f.hidden;
       const int nseg_max = f.n_shared + std::min(f.n_experts, R * f.top_k);
-      Phase r = gemv_phase(s.router, ACT_NORM, OUT_PART, R, G, 64);
+      Phase r = gemv_phase(s.router, ACT_NORM, OUT_PART, R, G, 64, R);  // every workgroup sums its splits
       r.layer = l;
       r.gain_off = s.ffn_norm.off;
       if (mk_status st = add_gemv(r, 0)) return st;
