@@ -1210,12 +1210,12 @@ __device__ __forceinline__ void gemv_sync(CArgs &a, const Phase &ph, char *smem)
   const int nrot = u1 - u0, r0 = rotated(ph) ? rot_start(s, ph.S, nrot) : 0;
   const bool fin = needs_finalise(ph);
   const bool direct_resid = ph.out == OUT_RESID && S_eff == 1;
-  // expert down products (a tile has one partial per (expert, k-split) and a workgroup many small units)
-  // and logits split over k (a workgroup has dozens of units, and a per-unit acknowledgement and counter
-  // round trip would outlast the unit's weights): contributions are counted once after all of this
-  // workgroup's units, and each tile is finalised by one designated workgroup (tile t by workgroup
-  // t mod G) once its count is complete
-  const bool deferred = fin && (expert || ph.out == OUT_LOGITS) && !direct_resid;
+  // expert down products (a tile has one partial per (expert, k-split) and a workgroup many small units),
+  // logits split over k and residual products split 8 or more ways (a workgroup has ten or more units,
+  // and a per-unit acknowledgement and counter round trip would outlast the unit's weights):
+  // contributions are counted once after all of this workgroup's units, and each tile is finalised by
+  // one designated workgroup (tile t by workgroup t mod G) once its count is complete
+  const bool deferred = fin && (expert || ph.out == OUT_LOGITS || ph.S >= 8) && !direct_resid;
   const bool swi = ph.out == OUT_PART && ph.stg_out;  // dense gate|up: SwiGLU of complete pairs, staged
   for (int unit = 0; unit < nrot; ++unit) {
     const int u = u0 + (r0 + unit < nrot ? r0 + unit : r0 + unit - nrot);
